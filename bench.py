@@ -1,0 +1,311 @@
+"""Benchmark of the fine-grained FP8 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of the workload, with
+the BF16 inputs already resident in HBM:
+  * prefill (default): quant_act_1x128(A 8192x7168) + quant_w_128x128(W
+    18432x7168) + gemm_fp8_blockscaled -> C 8192x18432 BF16;
+  * decode: the same three calls at A 64x7168;
+  * grouped_up: quant A 32768x7168, quant W 32x4096x7168, grouped GEMM;
+  * fused_down: fused_rmsnorm_quant(X 16384x7168) + quant A_down
+    16384x2048 + quant W 32x7168x2048 + grouped down-projection GEMM.
+Inputs rotate over several buffer sets so the 256 MB last-level cache
+cannot serve one step from the previous one.  `value` is whole-step GEMM
+throughput: GEMM FLOPs per step / step time.  Per-kernel durations come
+from HIP events recorded around each launch on the launch stream inside the
+timed region.  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quant GB/s (% HBM peak)"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "fine_grained_fp8_quant_amd", "csrc", "gemm.hip")
+QUANT_SOURCE = os.path.join(ROOT, "fine_grained_fp8_quant_amd", "csrc", "quant.hip")
+
+WORKLOAD_TITLES = {
+    "prefill": "dense prefill GEMM 8192x7168x18432 (A 1x128 + W 128x128 E4M3 quant + GEMM)",
+    "decode": "decode GEMM 64x7168x18432 (A 1x128 + W 128x128 E4M3 quant + GEMM)",
+    "grouped_up": "grouped MoE up-proj 32 experts, 32768 Zipf rows, K 7168, N 4096",
+    "fused_down": "fused RMSNorm+quant 16384x7168, grouped MoE down-proj 32 experts, 16384 rows, K 2048, N 7168",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TITLES))
+    p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 768 MB)")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Timer:
+    """HIP events around launches on the current stream, summed per name."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def run(self, name, fn):
+        import torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def avg_ms(self):
+        return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.pairs.items()}
+
+
+def build_sets(args):
+    """Device inputs and outputs for the chosen workload, several copies."""
+    import torch
+    from synth import make_workload
+    d = make_workload(args.workload, seed=args.seed)
+    sets = []
+    if args.workload in ("prefill", "decode"):
+        A, W = dev_bf16(d["A"]), dev_bf16(d["W"])
+        M, K, N = d["M"], d["K"], d["N"]
+        per_set = (A.numel() * 3 + W.numel() * 3 + M * N * 2)
+        flops = 2.0 * M * N * K
+        quant_bytes = {"quant_act_1x128": 3 * M * K + 4 * M * K // 128,
+                       "quant_w_128x128": 3 * N * K + 4 * N * K // 16384}
+        shape = {"M": M, "N": N, "K": K}
+    elif args.workload == "grouped_up":
+        A, W = dev_bf16(d["A"]), dev_bf16(d["W"])
+        R, K, N, E = d["R"], d["K"], d["N"], d["E"]
+        off = torch.from_numpy(d["offsets"]).cuda()
+        per_set = A.numel() * 3 + W.numel() * 3 + R * N * 2
+        flops = 2.0 * R * N * K
+        quant_bytes = {"quant_act_1x128": 3 * R * K + 4 * R * K // 128,
+                       "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
+        shape = {"E": E, "rows": R, "N": N, "K": K, "counts": d["counts"].tolist()}
+    else:
+        X, G = dev_bf16(d["X"]), dev_bf16(d["gamma"])
+        A, W = dev_bf16(d["A"]), dev_bf16(d["W"])
+        R, K, N, E = d["R"], d["K"], d["N"], d["E"]
+        Mx, Kx = d["Mx"], d["Kx"]
+        off = torch.from_numpy(d["offsets"]).cuda()
+        per_set = X.numel() * 3 + A.numel() * 3 + W.numel() * 3 + R * N * 2
+        flops = 2.0 * R * N * K
+        quant_bytes = {"fused_rmsnorm_quant": 3 * Mx * Kx + 4 * Mx * Kx // 128 + 2 * Kx,
+                       "quant_act_1x128": 3 * R * K + 4 * R * K // 128,
+                       "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
+        shape = {"Mx": Mx, "Kx": Kx, "E": E, "rows": R, "N": N, "K": K, "counts": d["counts"].tolist()}
+    n_sets = args.sets or max(2, int(np.ceil(768e6 / per_set)))
+    for i in range(n_sets):
+        s = {}
+        if args.workload in ("prefill", "decode", "grouped_up"):
+            s["A"] = A if i == 0 else A.clone()
+            s["W"] = W if i == 0 else W.clone()
+        else:
+            s["X"] = X if i == 0 else X.clone()
+            s["G"] = G
+            s["A"] = A if i == 0 else A.clone()
+            s["W"] = W if i == 0 else W.clone()
+        if args.workload in ("grouped_up", "fused_down"):
+            s["off"] = off
+        sets.append(s)
+    return d, sets, flops, quant_bytes, shape
+
+
+def make_step(args, fgq, d, n_sets):
+    """Allocates every output buffer up front; returns step(i, set, timer)
+    running the whole path once on input set i."""
+    import torch
+    eps = d.get("eps", 0.0)
+    outs = []
+    for _ in range(n_sets):
+        o = {}
+        if args.workload in ("prefill", "decode"):
+            M, K, N = d["M"], d["K"], d["N"]
+            o["qa"] = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+            o["sa"] = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+            o["qw"] = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+            o["sw"] = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+            o["c"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        else:
+            R, K, N, E = d["R"], d["K"], d["N"], d["E"]
+            if args.workload == "fused_down":
+                o["qx"] = torch.empty((d["Mx"], d["Kx"]), dtype=torch.uint8, device="cuda")
+                o["sx"] = torch.empty((d["Mx"], d["Kx"] // 128), dtype=torch.float32, device="cuda")
+            o["qa"] = torch.empty((R, K), dtype=torch.uint8, device="cuda")
+            o["sa"] = torch.empty((R, K // 128), dtype=torch.float32, device="cuda")
+            o["qw"] = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
+            o["sw"] = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda")
+            o["c"] = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+        outs.append(o)
+
+    def step(i, s, t):
+        o = outs[i]
+        if args.workload == "fused_down":
+            t.run("fused_rmsnorm_quant", lambda: fgq.fused_rmsnorm_quant(s["X"], s["G"], eps, q=o["qx"], s=o["sx"]))
+        t.run("quant_act_1x128", lambda: fgq.quant_act_1x128(s["A"], q=o["qa"], s=o["sa"]))
+        t.run("quant_w_128x128", lambda: fgq.quant_w_128x128(s["W"], q=o["qw"], s=o["sw"]))
+        if args.workload in ("prefill", "decode"):
+            t.run("gemm_fp8_blockscaled",
+                  lambda: fgq.gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"]))
+        else:
+            t.run("grouped_gemm_fp8_blockscaled",
+                  lambda: fgq.grouped_gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], s["off"],
+                                                           out=o["c"]))
+    return step
+
+
+def cpu_baseline(args, d):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    if args.workload in ("prefill", "decode"):
+        rows = min(d["M"], 1024)
+        cols = 4096
+        qa, sa = oracle.quant_act_1x128(d["A"][:rows])
+        qw, sw = oracle.quant_w_128x128(d["W"][:cols])
+        oracle.gemm_ref(qa, sa, qw, sw)
+        flops = 2.0 * rows * cols * d["K"]
+        sample = f"A rows 0..{rows - 1} x W rows 0..{cols - 1}, full K={d['K']}: quant A, quant W, float64 GEMM"
+    else:
+        e = int(np.argmax(d["counts"]))
+        r0 = int(d["offsets"][e])
+        rows = min(int(d["counts"][e]), 1024)
+        cols = min(d["N"], 4096)
+        if args.workload == "fused_down":
+            oracle.fused_rmsnorm_quant(d["X"][:rows], d["gamma"], d["eps"])
+        qa, sa = oracle.quant_act_1x128(d["A"][r0:r0 + rows])
+        qw, sw = oracle.quant_w_128x128(d["W"][e, :cols])
+        oracle.gemm_ref(qa, sa, qw, sw)
+        flops = 2.0 * rows * cols * d["K"]
+        sample = (f"expert {e}: {rows} rows x {cols} weight rows, full K={d['K']}"
+                  + (" (+ fused RMSNorm of as many rows)" if args.workload == "fused_down" else "")
+                  + ": quant, quant W, float64 GEMM")
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS",
+            "seconds": dt}
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if the kernel source is unchanged since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except Exception:
+        return None
+    entry = t.get(kernel)
+    if not entry:
+        return None
+    src = GEMM_SOURCE if "gemm" in kernel else QUANT_SOURCE
+    if entry.get("source_sha") != sha(src):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fine_grained_fp8_quant_amd as fgq
+    fgq.load_library()
+    torch.cuda.set_device(0)
+    print(f"[bench] building {args.workload} inputs", file=sys.stderr, flush=True)
+    d, sets, flops, quant_bytes, shape = build_sets(args)
+    step = make_step(args, fgq, d, len(sets))
+    warm = Timer()
+    for i in range(args.warmup):
+        step(i % len(sets), sets[i % len(sets)], warm)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps, {len(sets)} input sets)", file=sys.stderr, flush=True)
+    timer = Timer()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i % len(sets), sets[i % len(sets)], timer)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    kern = timer.avg_ms()
+    gemm_name = [k for k in kern if "gemm" in k][0]
+    gemm_ms = kern[gemm_name]
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    kernels = {}
+    for k, ms in kern.items():
+        if "gemm" in k:
+            kernels[k] = {"ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                          "frac_fp8_peak": flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        else:
+            gbs = quant_bytes[k] / (ms * 1e-3) / 1e9
+            kernels[k] = {"ms": ms, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                          "algorithmic_bytes": quant_bytes[k]}
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args, d)
+    line = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded, shapes and distributions of the named workload)",
+        "config": {"workload": WORKLOAD_TITLES[args.workload], **{k: v for k, v in shape.items() if k != "counts"},
+                   "input_sets": len(sets)},
+        "roofline": {"bound": "mfma", "kernel": gemm_name, "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
+                     "traffic": traffic_for(gemm_name)},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

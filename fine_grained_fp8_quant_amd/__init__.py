@@ -1,0 +1,276 @@
+"""Python binding of libfgq.so: fine-grained FP8 quantisation and the
+block-scaled FP8 GEMM on MI355X (gfx950).
+
+Argument marshalling only.  PyTorch supplies device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing, every call raises.
+
+Functions (same names as the C ABI in include/fgq.h, without the prefix):
+
+    quant_act_1x128(x)                     -> (q uint8 [M,K], s float32 [M,K/128])
+    quant_w_128x128(w)                     -> (q uint8 [N,K] or [B,N,K], s float32 [.., N/128, K/128])
+    fused_rmsnorm_quant(x, gamma, eps)     -> (q, s) as quant_act_1x128
+    gemm_fp8_blockscaled(qa, sa, qw, sw)   -> c bfloat16 [M, N]
+    grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets) -> c bfloat16 [R, N]
+
+Codes are returned as ``torch.uint8`` (``.view(torch.float8_e4m3fn)`` gives
+the FP8 dtype).  Scales may be any strided float32 view; the strides are
+passed to the kernels as they are.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FgqError", "load_library", "library_path", "lib",
+    "quant_act_1x128", "quant_w_128x128", "fused_rmsnorm_quant",
+    "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled", "gemm_workspace_bytes",
+    "debug_encode_e4m3", "debug_copy", "STATUS",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+STATUS = {
+    0: "FGQ_OK", 1: "FGQ_ERR_NULL", 2: "FGQ_ERR_SHAPE", 3: "FGQ_ERR_ALIGN",
+    4: "FGQ_ERR_STRIDE", 5: "FGQ_ERR_UNSUPPORTED", 6: "FGQ_ERR_HIP",
+}
+
+
+class FgqError(RuntimeError):
+    """A nonzero status from libfgq, or the library could not be loaded."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.environ.get("FGQ_LIB", os.path.join(_PKG_DIR, "libfgq.so"))
+
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_st = ctypes.c_int32
+
+_SIGNATURES = {
+    "fgq_quant_act_1x128": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp],
+    "fgq_quant_w_128x128": [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp],
+    "fgq_fused_rmsnorm_quant": [_vp, _i64, _vp, _f32, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp],
+    "fgq_gemm_fp8_blockscaled": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
+                                 _i64, _i64, _i64, _vp, ctypes.c_size_t, _vp],
+    "fgq_grouped_gemm_fp8_blockscaled": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                         _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp],
+    "fgq_gemm_workspace_bytes": [_i64, _i64, _i64],
+    "fgq_status_string": [_st],
+    "fgq_last_hip_error": [],
+    "fgq_abi_version": [],
+    "fgq_debug_encode_e4m3": [ctypes.c_uint32, _i64, _vp, _vp],
+    "fgq_debug_copy": [_vp, _vp, _i64, _vp],
+}
+_RESTYPES = {
+    "fgq_gemm_workspace_bytes": ctypes.c_size_t,
+    "fgq_status_string": ctypes.c_char_p,
+}
+
+lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libfgq.so (once) and declare its C signatures.  Raises FgqError if absent."""
+    global lib
+    if lib is not None:
+        return lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise FgqError(-1, f"libfgq.so not found at {path}; build it with "
+                           f"`python -m fine_grained_fp8_quant_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, _st)
+    lib = handle
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib.fgq_status_string(status).decode()
+        if status == 6:
+            msg += f" (hipError {lib.fgq_last_hip_error()})"
+        raise FgqError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, what):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected dtype {dtype}, got {t.dtype}")
+    if t.numel() > 0 and not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if t.dim() >= 1 and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{what}: the last dimension must be contiguous")
+
+
+def _need_scales(t, what):
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise TypeError(f"{what}: expected float32 scales, got {t.dtype}")
+    if t.numel() > 0 and not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+
+
+def _codes(t):
+    """Accept uint8 or float8_e4m3fn code tensors; return a uint8 view."""
+    torch = _torch()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    return t
+
+
+def quant_act_1x128(x, q=None, s=None, stream=None):
+    """1x128 tile quantisation of BF16 ``x [M, K]``.  Optional preallocated
+    outputs ``q`` (uint8 [M, K]) and ``s`` (float32 view of shape [M, K/128],
+    any strides)."""
+    torch = _torch()
+    load_library()
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _check(lib.fgq_quant_act_1x128(_ptr(x), x.stride(0), M, K, _ptr(q), q.stride(0), _ptr(s),
+                                   s.stride(0), s.stride(1), _stream(stream)))
+    return q, s
+
+
+def quant_w_128x128(w, q=None, s=None, stream=None):
+    """128x128 block quantisation of BF16 ``w [N, K]`` or ``[B, N, K]``."""
+    torch = _torch()
+    load_library()
+    _need(w, torch.bfloat16, "w")
+    batched = w.dim() == 3
+    w3 = w if batched else w.unsqueeze(0)
+    B, N, K = w3.shape
+    if q is None:
+        q = torch.empty((B, N, K), dtype=torch.uint8, device=w.device)
+    elif not batched:
+        q = q.unsqueeze(0)
+    if s is None:
+        s = torch.empty((B, N // 128, K // 128), dtype=torch.float32, device=w.device)
+    elif not batched:
+        s = s.unsqueeze(0)
+    _check(lib.fgq_quant_w_128x128(_ptr(w3), w3.stride(1), w3.stride(0), B, N, K, _ptr(q), q.stride(1),
+                                   q.stride(0), _ptr(s), s.stride(1), s.stride(2), s.stride(0),
+                                   _stream(stream)))
+    return (q, s) if batched else (q[0], s[0])
+
+
+def fused_rmsnorm_quant(x, gamma, eps: float, q=None, s=None, stream=None):
+    """RMSNorm(x; gamma, eps) in binary32 fused with 1x128 quantisation."""
+    torch = _torch()
+    load_library()
+    _need(x, torch.bfloat16, "x")
+    _need(gamma, torch.bfloat16, "gamma")
+    M, K = x.shape
+    if gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous [K] tensor")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _check(lib.fgq_fused_rmsnorm_quant(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(q),
+                                       q.stride(0), _ptr(s), s.stride(0), s.stride(1), _stream(stream)))
+    return q, s
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    load_library()
+    return int(lib.fgq_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_fp8_blockscaled(qa, sa, qw, sw, out=None, workspace=None, stream=None):
+    """``C = (dec(qa) * sa) @ (dec(qw) * sw).T`` with per-chunk FP32 promotion, BF16 out."""
+    torch = _torch()
+    load_library()
+    qa, qw = _codes(qa), _codes(qw)
+    _need(qa, torch.uint8, "qa")
+    _need(qw, torch.uint8, "qw")
+    _need_scales(sa, "sa")
+    _need_scales(sw, "sw")
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("qa and qw disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    need = gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qa.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.fgq_gemm_fp8_blockscaled(_ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1),
+                                        _ptr(qw), qw.stride(0), _ptr(sw), sw.stride(0), sw.stride(1),
+                                        _ptr(out), out.stride(0), M, N, K, _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
+    return out
+
+
+def grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets, out=None, stream=None):
+    """Ragged grouped GEMM: rows ``offsets[e]..offsets[e+1]`` of ``qa`` times expert
+    ``e``'s ``qw[e]``.  ``offsets`` is a device int32 tensor of E+1 entries."""
+    torch = _torch()
+    load_library()
+    qa, qw = _codes(qa), _codes(qw)
+    _need(qa, torch.uint8, "qa")
+    _need(qw, torch.uint8, "qw")
+    _need(offsets, torch.int32, "offsets")
+    _need_scales(sa, "sa")
+    _need_scales(sw, "sw")
+    R, K = qa.shape
+    E, N, K2 = qw.shape
+    if K2 != K:
+        raise ValueError("qa and qw disagree on K")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E + 1 entries")
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=qa.device)
+    _check(lib.fgq_grouped_gemm_fp8_blockscaled(
+        _ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(1),
+        qw.stride(0), _ptr(sw), sw.stride(1), sw.stride(2), sw.stride(0), _ptr(offsets), E, R,
+        _ptr(out), out.stride(0), N, K, _stream(stream)))
+    return out
+
+
+def debug_encode_e4m3(start: int, n: int, out=None, stream=None):
+    """Device E4M3 codes of clamp(float(bits), +-448) for bits = start .. start+n-1."""
+    torch = _torch()
+    load_library()
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _check(lib.fgq_debug_encode_e4m3(start & 0xFFFFFFFF, n, _ptr(out), _stream(stream)))
+    return out
+
+
+def debug_copy(src, dst, stream=None):
+    load_library()
+    _check(lib.fgq_debug_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), _stream(stream)))
+    return dst

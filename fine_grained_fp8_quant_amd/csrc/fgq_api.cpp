@@ -1,0 +1,181 @@
+// C ABI of libfgq.so (declared in include/fgq.h): host-side argument
+// validation, then a launch on the caller's stream.  Validation returns an
+// error code before any HIP call; nothing here allocates, synchronises or
+// reads device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fgq.h"
+#include "fgq_launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int64_t kMaxTiles = (int64_t)1 << 31;  // 32-bit tile indices in the kernels
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fgq_status_t from_hip(hipError_t e) {
+  if (e == hipSuccess) return FGQ_OK;
+  g_last_hip_error = (int32_t)e;
+  return FGQ_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Common checks for a [rows, K] BF16 input / E4M3 + scale output pair.
+fgq_status_t check_act_io(const void* x, int64_t ldx, int64_t M, int64_t K, const void* q, int64_t ldq,
+                          const float* s, int64_t s_sm, int64_t s_skb) {
+  if (M < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (K % 128 != 0) return FGQ_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return FGQ_OK;
+  if (!x || !q || !s) return FGQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FGQ_ERR_ALIGN;
+  if (ldx < K || ldx % 8 != 0 || ldq < K || ldq % 16 != 0) return FGQ_ERR_STRIDE;
+  if (s_sm < 0 || s_skb < 0) return FGQ_ERR_STRIDE;
+  if (M * (K / 128) >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
+  return FGQ_OK;
+}
+
+fgq_status_t check_gemm_common(const void* qa, int64_t lda, const float* sa, int64_t sa_sm, int64_t sa_skb,
+                               const void* qw, int64_t ldw, const float* sw, int64_t sw_snb,
+                               int64_t sw_skb, const void* c, int64_t ldc, int64_t N, int64_t K) {
+  if (!qa || !sa || !qw || !sw || !c) return FGQ_ERR_NULL;
+  if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sw, 4))
+    return FGQ_ERR_ALIGN;
+  if (lda < K || lda % 16 != 0 || ldw < K || ldw % 16 != 0 || ldc < N || ldc % 8 != 0)
+    return FGQ_ERR_STRIDE;
+  if (sa_sm < 0 || sa_skb < 0 || sw_snb < 0 || sw_skb < 0) return FGQ_ERR_STRIDE;
+  if (N / 128 > 65535) return FGQ_ERR_UNSUPPORTED;
+  return FGQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fgq_status_t fgq_quant_act_1x128(const void* x, int64_t ldx, int64_t M, int64_t K, void* q, int64_t ldq,
+                                 float* s, int64_t s_sm, int64_t s_skb, void* stream) {
+  const fgq_status_t st = check_act_io(x, ldx, M, K, q, ldq, s, s_sm, s_skb);
+  if (st != FGQ_OK || M == 0 || K == 0) return st;
+  return from_hip(fgq::launch_quant_act_1x128(static_cast<const uint16_t*>(x), ldx, M, K,
+                                              static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb,
+                                              as_stream(stream)));
+}
+
+fgq_status_t fgq_quant_w_128x128(const void* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N, int64_t K,
+                                 void* q, int64_t ldq, int64_t q_bs, float* s, int64_t s_snb,
+                                 int64_t s_skb, int64_t s_bs, void* stream) {
+  if (B < 0 || N < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0) return FGQ_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0 || K == 0) return FGQ_OK;
+  if (!w || !q || !s) return FGQ_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4)) return FGQ_ERR_ALIGN;
+  if (ldw < K || ldw % 8 != 0 || ldq < K || ldq % 16 != 0) return FGQ_ERR_STRIDE;
+  if (w_bs % 8 != 0 || q_bs % 16 != 0) return FGQ_ERR_STRIDE;
+  if (B > 1 && (w_bs < N * ldw || q_bs < N * ldq)) return FGQ_ERR_STRIDE;
+  if (s_snb < 0 || s_skb < 0 || s_bs < 0) return FGQ_ERR_STRIDE;
+  if (B * (N / 128) * (K / 128) >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
+  return from_hip(fgq::launch_quant_w_128x128(static_cast<const uint16_t*>(w), ldw, w_bs, B, N, K,
+                                              static_cast<uint8_t*>(q), ldq, q_bs, s, s_snb, s_skb, s_bs,
+                                              as_stream(stream)));
+}
+
+fgq_status_t fgq_fused_rmsnorm_quant(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M,
+                                     int64_t K, void* q, int64_t ldq, float* s, int64_t s_sm,
+                                     int64_t s_skb, void* stream) {
+  fgq_status_t st = check_act_io(x, ldx, M, K, q, ldq, s, s_sm, s_skb);
+  if (st != FGQ_OK || M == 0 || K == 0) return st;
+  if (K > 16384) return FGQ_ERR_UNSUPPORTED;
+  if (!gamma) return FGQ_ERR_NULL;
+  if (!aligned(gamma, 16)) return FGQ_ERR_ALIGN;
+  return from_hip(fgq::launch_fused_rmsnorm_quant(static_cast<const uint16_t*>(x), ldx,
+                                                  static_cast<const uint16_t*>(gamma), eps, M, K,
+                                                  static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb,
+                                                  as_stream(stream)));
+}
+
+size_t fgq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return fgq::gemm_workspace_bytes(M, N, K);
+}
+
+fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                                      int64_t sa_skb, const void* qw, int64_t ldw, const float* sw,
+                                      int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc, int64_t M,
+                                      int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || K == 0) return FGQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FGQ_OK;
+  fgq_status_t st = check_gemm_common(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, N, K);
+  if (st != FGQ_OK) return st;
+  if (M >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
+  const size_t need = fgq::gemm_workspace_bytes(M, N, K);
+  if (need > 0) {
+    if (!workspace) return FGQ_ERR_NULL;
+    if (workspace_bytes < need) return FGQ_ERR_SHAPE;
+    if (!aligned(workspace, 256)) return FGQ_ERR_ALIGN;
+  }
+  return from_hip(fgq::launch_gemm_fp8_blockscaled(
+      static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, sw,
+      sw_snb, sw_skb, static_cast<uint16_t*>(c), ldc, M, N, K, workspace, workspace_bytes,
+      as_stream(stream)));
+}
+
+fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                                              int64_t sa_skb, const void* qw, int64_t ldw, int64_t w_es,
+                                              const float* sw, int64_t sw_snb, int64_t sw_skb,
+                                              int64_t sw_es, const int32_t* offsets, int64_t E,
+                                              int64_t total_rows, void* c, int64_t ldc, int64_t N,
+                                              int64_t K, void* stream) {
+  if (E < 0 || total_rows < 0 || N < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || K == 0) return FGQ_ERR_UNSUPPORTED;
+  if (E > 65536 || total_rows >= ((int64_t)1 << 31) - 65536) return FGQ_ERR_UNSUPPORTED;
+  if (E == 0 || total_rows == 0 || N == 0) return FGQ_OK;
+  if (!offsets) return FGQ_ERR_NULL;
+  fgq_status_t st = check_gemm_common(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, N, K);
+  if (st != FGQ_OK) return st;
+  if (!aligned(offsets, 4)) return FGQ_ERR_ALIGN;
+  if (w_es % 16 != 0 || w_es < 0 || sw_es < 0) return FGQ_ERR_STRIDE;
+  if (E > 1 && w_es < N * ldw) return FGQ_ERR_STRIDE;
+  return from_hip(fgq::launch_grouped_gemm_fp8_blockscaled(
+      static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, w_es,
+      sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, static_cast<uint16_t*>(c), ldc, N, K,
+      as_stream(stream)));
+}
+
+const char* fgq_status_string(fgq_status_t status) {
+  switch (status) {
+    case FGQ_OK: return "ok";
+    case FGQ_ERR_NULL: return "a required pointer is NULL";
+    case FGQ_ERR_SHAPE: return "negative or inconsistent size";
+    case FGQ_ERR_ALIGN: return "pointer not aligned as documented";
+    case FGQ_ERR_STRIDE: return "leading dimension or stride too small or misaligned";
+    case FGQ_ERR_UNSUPPORTED: return "size not supported (K and N must be multiples of 128)";
+    case FGQ_ERR_HIP: return "HIP launch failed (see fgq_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int32_t fgq_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t fgq_abi_version(void) { return FGQ_ABI_VERSION; }
+
+fgq_status_t fgq_debug_encode_e4m3(uint32_t start, int64_t n, void* out, void* stream) {
+  if (n < 0 || n > ((int64_t)1 << 32)) return FGQ_ERR_SHAPE;
+  if (n == 0) return FGQ_OK;
+  if (!out) return FGQ_ERR_NULL;
+  return from_hip(fgq::launch_debug_encode_e4m3(start, n, static_cast<uint8_t*>(out), as_stream(stream)));
+}
+
+fgq_status_t fgq_debug_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0) return FGQ_ERR_SHAPE;
+  if (bytes == 0) return FGQ_OK;
+  if (!src || !dst) return FGQ_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0) return FGQ_ERR_ALIGN;
+  return from_hip(fgq::launch_debug_copy(src, dst, bytes, as_stream(stream)));
+}
+
+}  // extern "C"

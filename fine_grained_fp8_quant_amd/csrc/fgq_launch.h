@@ -1,0 +1,41 @@
+// Internal launch entry points behind the C ABI in include/fgq.h.  Arguments
+// have already been validated by fgq_api.cpp; each function only enqueues
+// work on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgq {
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                  int64_t ldq, float* s, int64_t s_sm, int64_t s_skb, hipStream_t st);
+
+hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N,
+                                  int64_t K, uint8_t* q, int64_t ldq, int64_t q_bs, float* s,
+                                  int64_t s_snb, int64_t s_skb, int64_t s_bs, hipStream_t st);
+
+hipError_t launch_fused_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                                      int64_t M, int64_t K, uint8_t* q, int64_t ldq, float* s,
+                                      int64_t s_sm, int64_t s_skb, hipStream_t st);
+
+hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                                       int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw,
+                                       int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc,
+                                       int64_t M, int64_t N, int64_t K, void* workspace,
+                                       size_t workspace_bytes, hipStream_t st);
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa,
+                                               int64_t sa_sm, int64_t sa_skb, const uint8_t* qw,
+                                               int64_t ldw, int64_t w_es, const float* sw,
+                                               int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+                                               const int32_t* offsets, int64_t E, int64_t total_rows,
+                                               uint16_t* c, int64_t ldc, int64_t N, int64_t K,
+                                               hipStream_t st);
+
+hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st);
+hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+
+}  // namespace fgq

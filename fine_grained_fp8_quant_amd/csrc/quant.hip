@@ -1,0 +1,252 @@
+// Online max-abs E4M3 quantisation kernels for gfx950:
+//   k_quant_act_1x128      one scale per 1x128 activation tile
+//   k_quant_w_128x128      one scale per 128x128 weight block (batched)
+//   k_fused_rmsnorm_quant  RMSNorm in binary32 fused with the 1x128 cast
+//
+// Source pages (no section numbers; located by page and paragraph):
+//   P1 "DeepSeek core readings" notes page (why-be.why-be.co.kr), paragraph 1:
+//      1x128 activation tiles, 128x128 weight blocks.
+//   P2 Q&A board page (xn--9g3bo1gtkw0l8ubf92bgle.kr), paragraphs 1, 3, 4: the
+//      quantisation reads 128 BF16 values from HBM and writes FP8 back; the
+//      scale maps the max-abs value onto the largest FP8 value and is derived
+//      online; normalisation stays in higher precision.
+//   P3 "How I Improved My Deepseek In In The Future" (youlimart.com),
+//      paragraph 3: fusing layer normalisation with the FP8 cast.
+//
+// All three are HBM-bound streaming kernels: 16-byte coalesced loads, a lane
+// group reduction for the max-abs, one correctly rounded division pair per
+// group, then multiply / clamp / hardware E4M3 convert.  This file is built
+// with -ffp-contract=off: the binary32 results must be bit-identical to the
+// written definition (no fused multiply-add anywhere).
+#include "fgq_device.h"
+#include "fgq_launch.h"
+
+namespace fgq {
+
+// ---------------------------------------------------------------------------
+// 1x128 activation tiles.  A tile is 256 bytes of BF16: 16 lanes x 16 bytes,
+// one DPP row.  A workgroup of 256 lanes owns 16 * kActU consecutive tiles
+// (row-major tile order, so a wave's loads are contiguous within a row) and
+// issues all of its loads before any arithmetic.
+constexpr int kActU = 4;
+
+__global__ __launch_bounds__(256) void k_quant_act_1x128(
+    const uint16_t* __restrict__ x, int64_t ldx, uint32_t KB, uint32_t n_tiles,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm, int64_t s_skb) {
+  const uint32_t lane16 = threadIdx.x & 15u;
+  const uint32_t grp = threadIdx.x >> 4;
+  const uint32_t base = blockIdx.x * (16u * kActU) + grp;
+  uint4 v[kActU];
+  uint32_t mm[kActU], kk[kActU];
+#pragma unroll
+  for (int u = 0; u < kActU; ++u) {
+    uint32_t t = base + 16u * u;
+    t = t < n_tiles ? t : n_tiles - 1u;  // clamped tail: loads stay in bounds
+    mm[u] = t / KB;
+    kk[u] = t - mm[u] * KB;
+    const uint16_t* p = x + (int64_t)mm[u] * ldx + kk[u] * 128u + lane16 * 8u;
+    v[u] = load_nt16(p);
+  }
+#pragma unroll
+  for (int u = 0; u < kActU; ++u) {
+    if (base + 16u * u >= n_tiles) break;  // uniform across each 16-lane row
+    float f[8];
+    unpack8(v[u], f);
+    const float a = max16(absmax8(f));
+    float sc, r;
+    group_scales(a, sc, r);
+    const uint2 o = cast8(f, r);
+    *reinterpret_cast<uint2*>(q + (int64_t)mm[u] * ldq + kk[u] * 128u + lane16 * 8u) = o;
+    if (lane16 == 0) s[(int64_t)mm[u] * s_sm + (int64_t)kk[u] * s_skb] = sc;
+  }
+}
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                  int64_t ldq, float* s, int64_t s_sm, int64_t s_skb, hipStream_t st) {
+  const uint32_t KB = (uint32_t)(K / 128);
+  const uint32_t n_tiles = (uint32_t)(M * KB);
+  const uint32_t grid = (n_tiles + 16u * kActU - 1) / (16u * kActU);
+  hipLaunchKernelGGL(k_quant_act_1x128, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, q, ldq, s,
+                     s_sm, s_skb);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks.  One workgroup per block: lane t reads 16 bytes of
+// rows (t/16) + 16p, p = 0..7, keeps the 64 values in registers, and the
+// block max-abs goes 16-lane DPP -> wave shuffle -> LDS across the 4 waves.
+__global__ __launch_bounds__(256) void k_quant_w_128x128(
+    const uint16_t* __restrict__ w, int64_t ldw, int64_t w_bs, uint32_t NB, uint32_t KB,
+    uint8_t* __restrict__ q, int64_t ldq, int64_t q_bs, float* __restrict__ s, int64_t s_snb,
+    int64_t s_skb, int64_t s_bs) {
+  __shared__ float red[4];
+  uint32_t id = blockIdx.x;
+  const uint32_t kb = id % KB;
+  id /= KB;
+  const uint32_t nb = id % NB;
+  const uint32_t b = id / NB;
+  const uint32_t c = threadIdx.x & 15u;
+  const uint32_t r0 = threadIdx.x >> 4;
+  const uint16_t* src = w + (int64_t)b * w_bs + ((int64_t)nb * 128 + r0) * ldw + kb * 128u + c * 8u;
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    v[p] = load_nt16(src + (int64_t)(16 * p) * ldw);
+  float m = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    float f[8];
+    unpack8(v[p], f);
+    m = fmaxf(m, absmax8(f));
+  }
+  m = max16(m);
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float sc, r;
+  group_scales(a, sc, r);
+  uint8_t* dst = q + (int64_t)b * q_bs + ((int64_t)nb * 128 + r0) * ldq + kb * 128u + c * 8u;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    float f[8];
+    unpack8(v[p], f);
+    *reinterpret_cast<uint2*>(dst + (int64_t)(16 * p) * ldq) = cast8(f, r);
+  }
+  if (threadIdx.x == 0) s[(int64_t)b * s_bs + (int64_t)nb * s_snb + (int64_t)kb * s_skb] = sc;
+}
+
+hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N,
+                                  int64_t K, uint8_t* q, int64_t ldq, int64_t q_bs, float* s,
+                                  int64_t s_snb, int64_t s_skb, int64_t s_bs, hipStream_t st) {
+  const uint32_t NB = (uint32_t)(N / 128), KB = (uint32_t)(K / 128);
+  const uint32_t grid = (uint32_t)(B * NB * KB);
+  hipLaunchKernelGGL(k_quant_w_128x128, dim3(grid), dim3(256), 0, st, w, ldw, w_bs, NB, KB, q, ldq,
+                     q_bs, s, s_snb, s_skb, s_bs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + 1x128 quantisation: one wave per row, the row held in
+// registers (NI 16-byte vectors per lane, lane l owning vectors l + 64 i).
+// That ownership is the summation order of the definition: lane l's partial
+// adds the squares of its vectors in turn, value by value, then a butterfly
+// over lane xor 32, 16, ..., 1.  In iteration i the lanes 16g..16g+15 hold
+// exactly tile 4i + g, so the tile max is a 16-lane DPP reduction.
+template <int NI>
+__global__ __launch_bounds__(256) void k_fused_rmsnorm_quant(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
+    uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm,
+    int64_t s_skb) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (row >= M) return;  // whole wave leaves together
+  const uint32_t V = K / 8u;
+  const uint16_t* xr = x + (int64_t)row * ldx;
+  uint4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t vi = lane + 64u * i;
+    if (vi < V) v[i] = load_nt16(xr + vi * 8u);
+    else v[i] = make_uint4(0, 0, 0, 0);
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (lane + 64u * i < V) {
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = acc + f[j] * f[j];  // contraction is off in this file
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d);
+  const float mean = acc / (float)K;
+  const float var = mean + eps;
+  const float rstd = 1.0f / sqrtf(var);
+  uint8_t* qr = q + (int64_t)row * ldq;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t vi = lane + 64u * i;
+    if (vi < V) {  // V is a multiple of 16: whole 16-lane rows
+      const uint4 gv = *reinterpret_cast<const uint4*>(gamma + vi * 8u);
+      float f[8], g[8], y[8];
+      unpack8(v[i], f);
+      unpack8(gv, g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = (f[j] * rstd) * g[j];
+      const float a = max16(absmax8(y));
+      float sc, r;
+      group_scales(a, sc, r);
+      *reinterpret_cast<uint2*>(qr + vi * 8u) = cast8(y, r);
+      if ((lane & 15u) == 0) s[(int64_t)row * s_sm + (int64_t)(vi >> 4) * s_skb] = sc;
+    }
+  }
+}
+
+hipError_t launch_fused_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                                      int64_t M, int64_t K, uint8_t* q, int64_t ldq, float* s,
+                                      int64_t s_sm, int64_t s_skb, hipStream_t st) {
+  const uint32_t grid = (uint32_t)((M + 3) / 4);
+  const int64_t ni = (K / 8 + 63) / 64;
+  if (ni <= 4)
+    hipLaunchKernelGGL(k_fused_rmsnorm_quant<4>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
+                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  else if (ni <= 8)
+    hipLaunchKernelGGL(k_fused_rmsnorm_quant<8>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
+                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  else if (ni <= 16)
+    hipLaunchKernelGGL(k_fused_rmsnorm_quant<16>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
+                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  else
+    hipLaunchKernelGGL(k_fused_rmsnorm_quant<32>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
+                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostics.
+__global__ __launch_bounds__(256) void k_debug_encode_e4m3(uint32_t start, uint64_t n,
+                                                           uint8_t* __restrict__ out) {
+  const uint64_t i0 = ((uint64_t)blockIdx.x * 256u + threadIdx.x) * 4u;
+  if (i0 >= n) return;
+  float f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[j] = clamp448(__uint_as_float(start + (uint32_t)(i0 + j)));
+  const uint32_t w = e4m3x4(f[0], f[1], f[2], f[3]);
+  if (i0 + 4 <= n) {
+    uint8_t* p = out + i0;
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) == 0) {
+      *reinterpret_cast<uint32_t*>(p) = w;
+      return;
+    }
+  }
+  for (int j = 0; j < 4 && i0 + j < n; ++j) out[i0 + j] = (uint8_t)(w >> (8 * j));
+}
+
+hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st) {
+  const uint64_t threads = ((uint64_t)n + 3) / 4;
+  const uint32_t grid = (uint32_t)((threads + 255) / 256);
+  hipLaunchKernelGGL(k_debug_encode_e4m3, dim3(grid), dim3(256), 0, st, start, (uint64_t)n, out);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_debug_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                    uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  const uint64_t n16 = (uint64_t)bytes / 16;
+  uint64_t grid = (n16 + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  if (grid == 0) grid = 1;
+  hipLaunchKernelGGL(k_debug_copy, dim3((uint32_t)grid), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace fgq

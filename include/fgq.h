@@ -1,0 +1,213 @@
+/*
+ * fgq.h -- fine-grained FP8 quantisation and block-scaled FP8 GEMM for
+ * AMD Instinct MI355X (gfx950).  C ABI of libfgq.so.
+ *
+ * The method (DeepSeek-V3 FP8 mixed precision, as described on the source
+ * pages; they have no section numbers, so passages are located by page and
+ * paragraph):
+ *   P1  "DeepSeek core readings" notes page (why-be.why-be.co.kr)
+ *   P2  Q&A board page (xn--9g3bo1gtkw0l8ubf92bgle.kr)
+ *   P3  "How I Improved My Deepseek In In The Future" (youlimart.com)
+ *   P4  "How Google Is Changing How We Method Deepseek" (xn--jj0bz6z98ct0a29q.com)
+ *
+ * FP8 format: OCP E4M3 ("E4M3FN"; bias 7, largest finite 448, NaN 0x7F/0xFF).
+ * Codes are stored as one byte each.  Scales are IEEE binary32 and are the
+ * dequantisation multipliers: value ~= decode(code) * scale.
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is a DEVICE pointer on the calling thread's current
+ *     HIP device.  The caller allocates and frees every buffer; the library
+ *     never allocates, frees, synchronises, or reads device data on the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued on it, in stream order; calls return before the
+ *     GPU work completes.  Asynchronous faults surface at the caller's next
+ *     synchronisation.
+ *   - Leading dimensions (ld*) and strides are in ELEMENTS of the pointed-to
+ *     type (BF16 = 2 bytes, E4M3 = 1 byte, float = 4 bytes).  Row-major,
+ *     with the K (inner) dimension contiguous.
+ *   - Arguments are validated on the host before any HIP call.  On an error
+ *     nothing is enqueued and a status > 0 is returned.  A call with an empty
+ *     problem (M == 0, rows == 0, B == 0 or E == 0) returns FGQ_OK and
+ *     launches nothing.
+ *   - Not checked (undefined behaviour): outputs that alias inputs or each
+ *     other; NaN or Inf inputs; device data that breaks a documented
+ *     invariant (e.g. grouped offsets).
+ *   - Thread-safe: the library holds no mutable global state other than a
+ *     thread-local copy of the last HIP error code.
+ */
+#ifndef FGQ_H
+#define FGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fgq_status_t;
+
+enum {
+  FGQ_OK = 0,
+  FGQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  FGQ_ERR_SHAPE = 2,       /* a negative size, or an inconsistent shape */
+  FGQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+  FGQ_ERR_STRIDE = 4,      /* a leading dimension / stride is too small or misaligned */
+  FGQ_ERR_UNSUPPORTED = 5, /* sizes outside what the kernels support (e.g. K % 128 != 0) */
+  FGQ_ERR_HIP = 6          /* a HIP launch failed; see fgq_last_hip_error() */
+};
+
+#define FGQ_ABI_VERSION 1
+
+/*
+ * fgq_quant_act_1x128 -- online activation quantisation, one scale per
+ * 1x128 tile (per token per 128 channels) [P1 paragraph 1], derived from the
+ * tile's max-abs value mapped onto the largest E4M3 value [P2 paragraphs 3-4,
+ * P4 paragraph 1].
+ *
+ * For every row m < M and tile kb < K/128, with x_j the 128 BF16 inputs of the
+ * tile widened exactly to binary32:
+ *     a = max_j |x_j|
+ *     s = fl32(a / 448)                       (stored scale)
+ *     r = min(fl32(448 / a), FLT_MAX)         (a = 0 gives FLT_MAX)
+ *     q_j = E4M3_rne(clamp(fl32(x_j * r), -448, 448))
+ * All binary32 operations round to nearest even; subnormals are kept; the
+ * sign of zero is kept.  Results are bit-identical to that definition.
+ *
+ *   x      BF16 [M, K], row stride ldx (>= K, multiple of 8); 16-byte aligned.
+ *   q      E4M3 [M, K] output, row stride ldq (>= K, multiple of 16); 16-byte aligned.
+ *   s      float output, s[m * s_sm + kb * s_skb]; 4-byte aligned; s_sm, s_skb >= 0
+ *          and the M x K/128 positions must not overlap (not checked).
+ *   K must be a multiple of 128.  M >= 0.
+ */
+fgq_status_t fgq_quant_act_1x128(const void* x, int64_t ldx, int64_t M, int64_t K,
+                                 void* q, int64_t ldq, float* s, int64_t s_sm, int64_t s_skb,
+                                 void* stream);
+
+/*
+ * fgq_quant_w_128x128 -- weight quantisation, one scale per 128x128 block
+ * (per 128 input channels per 128 output channels) [P1 paragraph 1], same
+ * scale rule as fgq_quant_act_1x128 with the tile replaced by the block.
+ * Batched over B experts (B = 1 for a dense weight).
+ *
+ *   w      BF16 [B][N, K]; w[b*w_bs + n*ldw + k]; ldw >= K, multiple of 8;
+ *          w_bs multiple of 8; 16-byte aligned.
+ *   q      E4M3 [B][N, K]; q[b*q_bs + n*ldq + k]; ldq >= K, multiple of 16;
+ *          q_bs multiple of 16; 16-byte aligned.
+ *   s      float [B][N/128][K/128]; s[b*s_bs + nb*s_snb + kb*s_skb]; strides >= 0.
+ *   N and K must be multiples of 128.  B >= 0.
+ */
+fgq_status_t fgq_quant_w_128x128(const void* w, int64_t ldw, int64_t w_bs, int64_t B,
+                                 int64_t N, int64_t K, void* q, int64_t ldq, int64_t q_bs,
+                                 float* s, int64_t s_snb, int64_t s_skb, int64_t s_bs,
+                                 void* stream);
+
+/*
+ * fgq_fused_rmsnorm_quant -- RMSNorm fused with the 1x128 FP8 cast, so the
+ * normalised row never makes a BF16 round trip through HBM [P3 paragraph 3,
+ * P2 paragraph 1].  The norm is computed in binary32 and is not rounded to
+ * BF16 before the cast:
+ *     y_k = fl32(fl32(x_k * rstd) * gamma_k),
+ *     rstd = fl32(1 / fl32(sqrt(fl32(fl32(ss / K) + eps))))
+ * where ss is the sum of x_k^2 in one fixed order: the row is cut into
+ * 8-value vectors; partial sum l (l = 0..63) takes vectors l, l+64, ... in
+ * turn and adds their squares one value at a time (no fused multiply-add);
+ * the 64 partials are combined by adding partial (l xor d) for
+ * d = 32, 16, 8, 4, 2, 1.  Then y is quantised exactly as in
+ * fgq_quant_act_1x128.  Results are bit-identical to that definition.
+ *
+ *   x      BF16 [M, K], row stride ldx (>= K, multiple of 8); 16-byte aligned.
+ *   gamma  BF16 [K]; 16-byte aligned.
+ *   eps    binary32 epsilon (the caller rounds it to float).
+ *   q, s   as in fgq_quant_act_1x128.
+ *   K must be a multiple of 128 and at most 16384.
+ */
+fgq_status_t fgq_fused_rmsnorm_quant(const void* x, int64_t ldx, const void* gamma, float eps,
+                                     int64_t M, int64_t K, void* q, int64_t ldq,
+                                     float* s, int64_t s_sm, int64_t s_skb, void* stream);
+
+/*
+ * fgq_gemm_fp8_blockscaled -- C = A_hat * W_hat^T in FP8 with per-group K
+ * scaling [P2 paragraph 3]: for each 128-wide K chunk kb the FP8 products are
+ * summed by the matrix cores, and the partial sum is promoted into a binary32
+ * accumulator multiplied by sa[m, kb] * sw[n/128, kb] [P2 paragraph 3,
+ * P4 paragraph 4, P1 paragraph 4]; the result is rounded to BF16 (nearest even).
+ *
+ *   qa     E4M3 [M, K] (1x128-quantised activations), row stride lda (>= K,
+ *          multiple of 16); 16-byte aligned.
+ *   sa     float, sa[m * sa_sm + kb * sa_skb].
+ *   qw     E4M3 [N, K] (128x128-quantised weights), row stride ldw (>= K,
+ *          multiple of 16); 16-byte aligned.
+ *   sw     float, sw[nb * sw_snb + kb * sw_skb].
+ *   c      BF16 [M, N] output, row stride ldc (>= N, multiple of 8); 16-byte aligned.
+ *   workspace / workspace_bytes: scratch the caller provides; at least
+ *          fgq_gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned (may be
+ *          NULL when that is 0).
+ *   N and K must be multiples of 128.  M >= 0 (any value; M = 0 launches nothing).
+ * The result is within the tolerance of the float64 definition (summation
+ * order inside a chunk is the matrix core's; not bit-reproducible across
+ * tile configurations).
+ */
+fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                                      int64_t sa_skb, const void* qw, int64_t ldw, const float* sw,
+                                      int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc,
+                                      int64_t M, int64_t N, int64_t K, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fgq_gemm_fp8_blockscaled needs for this shape (0 = none). */
+size_t fgq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * fgq_grouped_gemm_fp8_blockscaled -- the ragged grouped variant for MoE
+ * experts, whose up-projection forward GEMMs run in FP8 [P2 paragraph 4,
+ * P3 paragraph 4].  Rows of A are concatenated by expert: expert e owns rows
+ * offsets[e] .. offsets[e+1]-1 and multiplies them by its own weight
+ *     W_e = qw + e * w_es,  scales sw + e * sw_es,
+ * with the same per-chunk promotion as fgq_gemm_fp8_blockscaled.  Experts
+ * with no rows cost nothing.
+ *
+ *   offsets    DEVICE int32 [E + 1], non-decreasing, offsets[0] = 0,
+ *              offsets[E] = total_rows.  Read only by the GPU (no host sync).
+ *              Rows outside [0, total_rows) are never read or written even if
+ *              offsets break this invariant; what is then computed is undefined.
+ *   qa, sa     as in the dense GEMM, with total_rows rows.
+ *   qw         E4M3 [E][N, K]; w_es (elements) multiple of 16.
+ *   sw         float; sw[e * sw_es + nb * sw_snb + kb * sw_skb].
+ *   c          BF16 [total_rows, N].
+ *   E >= 0 and at most 65536.  N and K multiples of 128.
+ */
+fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa,
+                                              int64_t sa_sm, int64_t sa_skb, const void* qw,
+                                              int64_t ldw, int64_t w_es, const float* sw,
+                                              int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+                                              const int32_t* offsets, int64_t E, int64_t total_rows,
+                                              void* c, int64_t ldc, int64_t N, int64_t K,
+                                              void* stream);
+
+/* Text for a status code (static storage; never NULL). */
+const char* fgq_status_string(fgq_status_t status);
+
+/* The hipError_t behind this thread's last FGQ_ERR_HIP (0 if none). */
+int32_t fgq_last_hip_error(void);
+
+/* FGQ_ABI_VERSION of the loaded library. */
+int32_t fgq_abi_version(void);
+
+/*
+ * Diagnostics used by the tests and the benchmark (not part of the method).
+ *
+ * fgq_debug_encode_e4m3 -- out[i] = E4M3 code of clamp(float(bits = start + i), -448, 448)
+ * through the same device conversion the quantisation kernels use, i < n.
+ * Bit patterns that are NaN give unspecified codes.  out: device, n bytes.
+ */
+fgq_status_t fgq_debug_encode_e4m3(uint32_t start, int64_t n, void* out, void* stream);
+
+/* fgq_debug_copy -- plain device copy of `bytes` bytes (16-byte aligned
+ * pointers, bytes a multiple of 16); used to calibrate traffic counters. */
+fgq_status_t fgq_debug_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGQ_H */

@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fgq.h declares, and rejects bad arguments on the host before any HIP
+call (so these run on a machine with no GPU).  Empty problems return FGQ_OK
+and launch nothing."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fgq.h")
+
+OK, NULL, SHAPE, ALIGN, STRIDE, UNSUP = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fine_grained_fp8_quant_amd as fgq
+    if not os.path.exists(fgq.library_path()):
+        from fine_grained_fp8_quant_amd.build import build
+        build()
+    return fgq.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fgq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("fgq_quant_act_1x128", "fgq_quant_w_128x128", "fgq_fused_rmsnorm_quant",
+              "fgq_gemm_fp8_blockscaled", "fgq_grouped_gemm_fp8_blockscaled"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.fgq_abi_version() == 1
+    for code in range(7):
+        assert lib.fgq_status_string(code)
+    assert lib.fgq_status_string(99) == b"unknown status"
+    assert lib.fgq_last_hip_error() == 0
+
+
+P = 1 << 20          # a fake, 16-byte aligned "device" address: never dereferenced on error paths
+Q = P + 4096
+S = P + 8192
+
+
+def act(lib, x=P, ldx=256, M=4, K=256, q=Q, ldq=256, s=S, s_sm=2, s_skb=1):
+    return lib.fgq_quant_act_1x128(x, ldx, M, K, q, ldq, s, s_sm, s_skb, None)
+
+
+def test_quant_act_validation(lib):
+    assert act(lib, M=-1) == SHAPE
+    assert act(lib, K=100) == UNSUP
+    assert act(lib, M=0) == OK                      # empty: nothing launched
+    assert act(lib, x=0) == NULL
+    assert act(lib, q=0) == NULL
+    assert act(lib, s=0) == NULL
+    assert act(lib, x=P + 2) == ALIGN
+    assert act(lib, q=Q + 8) == ALIGN
+    assert act(lib, s=S + 2) == ALIGN
+    assert act(lib, ldx=128) == STRIDE
+    assert act(lib, ldx=260) == STRIDE
+    assert act(lib, ldq=264) == STRIDE
+    assert act(lib, s_sm=-1) == STRIDE
+
+
+def wq(lib, w=P, ldw=256, w_bs=256 * 128, B=2, N=128, K=256, q=Q, ldq=256, q_bs=256 * 128, s=S,
+       s_snb=2, s_skb=1, s_bs=2):
+    return lib.fgq_quant_w_128x128(w, ldw, w_bs, B, N, K, q, ldq, q_bs, s, s_snb, s_skb, s_bs, None)
+
+
+def test_quant_w_validation(lib):
+    assert wq(lib, B=-1) == SHAPE
+    assert wq(lib, N=100) == UNSUP
+    assert wq(lib, K=64) == UNSUP
+    assert wq(lib, B=0) == OK
+    assert wq(lib, w=0) == NULL
+    assert wq(lib, w=P + 8) == ALIGN
+    assert wq(lib, w_bs=100) == STRIDE               # overlapping experts
+    assert wq(lib, q_bs=256 * 128 - 16) == STRIDE
+    assert wq(lib, ldq=256 + 8) == STRIDE
+
+
+def test_fused_validation(lib):
+    f = lib.fgq_fused_rmsnorm_quant
+    assert f(P, 256, 0, ctypes.c_float(1e-6), 4, 256, Q, 256, S, 2, 1, None) == NULL
+    assert f(P, 256, Q + 4, ctypes.c_float(1e-6), 4, 256, Q, 256, S, 2, 1, None) == ALIGN
+    assert f(P, 32768, Q, ctypes.c_float(1e-6), 4, 32768, Q, 32768, S, 256, 1, None) == UNSUP
+    assert f(P, 256, Q, ctypes.c_float(1e-6), 0, 256, Q, 256, S, 2, 1, None) == OK
+
+
+def gemm(lib, qa=P, lda=256, sa=S, sa_sm=2, sa_skb=1, qw=Q, ldw=256, sw=S, sw_snb=2, sw_skb=1, c=Q,
+         ldc=256, M=4, N=256, K=256, ws=0, ws_bytes=0):
+    return lib.fgq_gemm_fp8_blockscaled(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc,
+                                        M, N, K, ws, ws_bytes, None)
+
+
+def test_gemm_validation(lib):
+    assert gemm(lib, M=-1) == SHAPE
+    assert gemm(lib, N=100) == UNSUP
+    assert gemm(lib, K=0) == UNSUP
+    assert gemm(lib, K=200) == UNSUP
+    assert gemm(lib, M=0) == OK
+    assert gemm(lib, N=0) == OK
+    assert gemm(lib, qa=0) == NULL
+    assert gemm(lib, sw=0) == NULL
+    assert gemm(lib, c=Q + 2) == ALIGN
+    assert gemm(lib, sa=S + 1) == ALIGN
+    assert gemm(lib, lda=128) == STRIDE
+    assert gemm(lib, ldw=264) == STRIDE
+    assert gemm(lib, ldc=128) == STRIDE
+    assert gemm(lib, sa_skb=-1) == STRIDE
+    assert lib.fgq_gemm_workspace_bytes(0, 256, 256) == 0
+
+
+def grouped(lib, E=4, R=100, offsets=S, w_es=256 * 256, N=256, K=256, qa=P, ldc=256):
+    return lib.fgq_grouped_gemm_fp8_blockscaled(qa, 256, S, 2, 1, Q, 256, w_es, S, 2, 1, 4, offsets, E, R,
+                                                Q, ldc, N, K, None)
+
+
+def test_grouped_validation(lib):
+    assert grouped(lib, E=-1) == SHAPE
+    assert grouped(lib, R=-1) == SHAPE
+    assert grouped(lib, E=70000) == UNSUP
+    assert grouped(lib, K=100) == UNSUP
+    assert grouped(lib, E=0) == OK
+    assert grouped(lib, R=0) == OK
+    assert grouped(lib, offsets=0) == NULL
+    assert grouped(lib, qa=0) == NULL
+    assert grouped(lib, offsets=S + 2) == ALIGN
+    assert grouped(lib, w_es=100 * 16) == STRIDE
+    assert grouped(lib, ldc=128) == STRIDE
+
+
+def test_debug_validation(lib):
+    assert lib.fgq_debug_encode_e4m3(0, -1, P, None) == SHAPE
+    assert lib.fgq_debug_encode_e4m3(0, 0, 0, None) == OK
+    assert lib.fgq_debug_encode_e4m3(0, 16, 0, None) == NULL
+    assert lib.fgq_debug_copy(P, Q, 15, None) == ALIGN
+    assert lib.fgq_debug_copy(P + 1, Q, 16, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+    import fine_grained_fp8_quant_amd as fgq
+    monkeypatch.setenv("FGQ_LIB", str(tmp_path / "missing.so"))
+    saved = fgq.lib
+    try:
+        fgq.lib = None
+        with pytest.raises(fgq.FgqError):
+            fgq.load_library()
+    finally:
+        fgq.lib = saved
+    importlib.invalidate_caches()

@@ -1,0 +1,213 @@
+"""GPU parity of the block-scaled FP8 GEMM and its grouped variant.
+
+Gate (from the workload definition): normwise relative error <= 2e-3 against
+the oracle's float64 result from the same dequantised operands, and
+elementwise <= 1e-2 relative wherever |ref| > 1e-2 * rms(ref).
+
+  * exact pin: integer-valued codes with power-of-two scales make every
+    partial sum exact in binary32, so the GPU result must equal the oracle's
+    result rounded to BF16, bit for bit, at K = 7168;
+  * one-hot rows pin the scale indexing across tiles;
+  * the tolerance gate on every workload: whole problems at reduced rows
+    (operands quantised by the oracle, so the GEMM is tested on its own),
+    and the full sizes in the benchmark's launch configuration, quantised on
+    the GPU and checked on sampled rows against the oracle's own
+    quantisation and product;
+  * ragged M, K = 128, strided operands, guard bands around C;
+  * grouped: empty experts, one expert holding every row, single-row
+    experts, counts that are not multiples of the tile, E = 1 equals dense.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_workload, normal_bf16, rng_for
+from tests.gpu_util import Guarded, dev_bf16, dev_f32, dev_u8, host_bf16_f64, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None):
+    import torch
+    M, K = qa.shape
+    N = qw.shape[0]
+    if lda is not None:
+        pad = np.zeros((M, lda), np.uint8)
+        pad[:, :K] = qa
+        qa_d = dev_u8(pad)[:, :K]
+    else:
+        qa_d = dev_u8(qa)
+    cg = Guarded(M, N, torch.bfloat16, ld=ldc)
+    fgq.gemm_fp8_blockscaled(qa_d, dev_f32(sa), dev_u8(qw), dev_f32(sw), out=cg.view)
+    torch.cuda.synchronize()
+    cg.check_canaries()
+    return host_bf16_f64(cg.view)
+
+
+def _gate(c, ref, what):
+    g = oracle.gemm_gate(c, ref)
+    floor = oracle.gemm_gate(oracle.bf16_round_f64(ref), ref)["normwise"]
+    log(f"{what}: normwise {g['normwise']:.3e} (bf16 floor {floor:.3e}), max elem {g['max_elem_rel']:.3e}")
+    assert g["ok"], (what, g)
+    return g
+
+
+def _int_codes(shape, rng):
+    ints = rng.integers(-8, 9, size=shape)
+    table = {0: 0}
+    for v in range(1, 9):
+        e = int(math.floor(math.log2(v)))
+        table[v] = ((e + 7) << 3) | int((v / 2 ** e - 1) * 8)
+        table[-v] = table[v] | 0x80
+    lut = np.array([table[v] for v in range(-8, 9)], dtype=np.uint8)
+    return lut[ints + 8]
+
+
+def test_gemm_integer_codes_bit_exact(fgq_gpu):
+    rng = np.random.default_rng(0)
+    M, N, K = 200, 384, 7168
+    qa, qw = _int_codes((M, K), rng), _int_codes((N, K), rng)
+    sa = (2.0 ** rng.integers(-1, 2, (M, K // 128))).astype(np.float32)
+    sw = (2.0 ** rng.integers(-1, 2, (N // 128, K // 128))).astype(np.float32)
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    c = _gemm(fgq_gpu, qa, sa, qw, sw)
+    assert np.array_equal(c, oracle.bf16_round_f64(ref))
+
+
+def test_gemm_one_hot_scale_indexing(fgq_gpu):
+    rng = np.random.default_rng(1)
+    M, N, K = 150, 512, 1024
+    qa = np.zeros((M, K), np.uint8)
+    ks = rng.integers(0, K, M)
+    qa[np.arange(M), ks] = 0x38
+    qw = np.full((N, K), 0x38, np.uint8)
+    sa = rng.uniform(0.5, 2, (M, K // 128)).astype(np.float32)
+    sw = rng.uniform(0.5, 2, (N // 128, K // 128)).astype(np.float32)
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    c = _gemm(fgq_gpu, qa, sa, qw, sw)
+    # one product per output: exact up to the rounding of sa*sw and the BF16 output
+    assert np.all(np.abs(c - ref) <= np.abs(ref) * (2.0 ** -8 + 2.0 ** -22))
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldc", [(1, 128, 128, None, None), (129, 256, 384, None, None),
+                                           (300, 384, 1024, 1040, 392), (64, 128, 7168, None, None),
+                                           (255, 640, 2048, None, 648)])
+def test_gemm_shapes_oracle_operands(fgq_gpu, M, N, K, lda, ldc):
+    a = normal_bf16((M, K), 1.0, rng_for(5, M))
+    w = normal_bf16((N, K), 0.02, rng_for(5, N + 1))
+    qa, sa = oracle.quant_act_1x128(a)
+    qw, sw = oracle.quant_w_128x128(w)
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    c = _gemm(fgq_gpu, qa, sa, qw, sw, ldc=ldc, lda=lda)
+    _gate(c, ref, f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("decode", None), ("prefill", 384)])
+def test_gemm_workloads_oracle_operands(fgq_gpu, name, rows):
+    d = make_workload(name, rows=rows)
+    qa, sa = oracle.quant_act_1x128(d["A"])
+    qw, sw = oracle.quant_w_128x128(d["W"])
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    c = _gemm(fgq_gpu, qa, sa, qw, sw)
+    _gate(c, ref, f"gemm {name}")
+    # reported, not gated: distance to the unquantised BF16 product
+    a64 = oracle.f32_from_bf16(d["A"]).astype(np.float64)
+    w64 = oracle.f32_from_bf16(d["W"]).astype(np.float64)
+    exact = a64 @ w64.T
+    log(f"  vs unquantised BF16 operands: normwise {np.linalg.norm(c - exact) / np.linalg.norm(exact):.3e}")
+
+
+def test_gemm_prefill_full_size_sampled(fgq_gpu):
+    """8192x7168x18432 end to end on the GPU (quantise A and W, GEMM) as the
+    benchmark runs it; 192 sampled rows against the oracle's own
+    quantisation and float64 product."""
+    import torch
+    d = make_workload("prefill")
+    A, W = d["A"], d["W"]
+    qa, sa = fgq_gpu.quant_act_1x128(dev_bf16(A))
+    qw, sw = fgq_gpu.quant_w_128x128(dev_bf16(W))
+    c = fgq_gpu.gemm_fp8_blockscaled(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(2).choice(A.shape[0], 192, replace=False))
+    rows[0], rows[-1] = 0, A.shape[0] - 1
+    qao, sao = oracle.quant_act_1x128(A[rows])
+    qwo, swo = oracle.quant_w_128x128(W)
+    ref = oracle.gemm_ref(qao, sao, qwo, swo)
+    _gate(host_bf16_f64(c[rows.tolist()]), ref, "prefill full (sampled rows)")
+
+
+# ------------------------------------------------------------------ grouped
+
+def _grouped(fgq, qa, sa, qw, sw, offsets):
+    import torch
+    R = qa.shape[0]
+    N = qw.shape[1]
+    cg = Guarded(R, N, torch.bfloat16)
+    fgq.grouped_gemm_fp8_blockscaled(dev_u8(qa), dev_f32(sa), dev_u8(qw), dev_f32(sw),
+                                     torch.from_numpy(np.asarray(offsets, np.int32)).cuda(), out=cg.view)
+    torch.cuda.synchronize()
+    cg.check_canaries()
+    return host_bf16_f64(cg.view)
+
+
+@pytest.mark.parametrize("counts", [[0, 200, 0, 57], [300, 0, 0, 0], [1, 1, 1, 130], [0, 0, 0, 5],
+                                    [129, 127, 128, 256]])
+def test_grouped_ragged_counts(fgq_gpu, counts):
+    E, N, K = len(counts), 256, 512
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    a = normal_bf16((R, K), 1.0, rng_for(6, R))
+    w = normal_bf16((E, N, K), 0.02, rng_for(6, 7))
+    qa, sa = oracle.quant_act_1x128(a)
+    qw, sw = oracle.quant_w_128x128(w)
+    ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
+    c = _grouped(fgq_gpu, qa, sa, qw, sw, off)
+    _gate(c, ref, f"grouped {counts}")
+
+
+def test_grouped_single_expert_equals_dense(fgq_gpu):
+    M, N, K = 333, 384, 1024
+    a = normal_bf16((M, K), 1.0, rng_for(7, 1))
+    w = normal_bf16((1, N, K), 0.02, rng_for(7, 2))
+    qa, sa = oracle.quant_act_1x128(a)
+    qw, sw = oracle.quant_w_128x128(w)
+    g = _grouped(fgq_gpu, qa, sa, qw, sw, [0, M])
+    d = _gemm(fgq_gpu, qa, sa, qw[0], sw[0])
+    assert np.array_equal(g, d)
+
+
+@pytest.mark.parametrize("name", ["grouped_up", "fused_down"])
+def test_grouped_workloads_reduced_rows(fgq_gpu, name):
+    d = make_workload(name, rows=1500)
+    qa, sa = oracle.quant_act_1x128(d["A"])
+    qw, sw = oracle.quant_w_128x128(d["W"])
+    ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, d["offsets"])
+    c = _grouped(fgq_gpu, qa, sa, qw, sw, d["offsets"])
+    _gate(c, ref, f"{name} rows={d['R']} counts={d['counts'].tolist()}")
+
+
+@pytest.mark.parametrize("name", ["grouped_up", "fused_down"])
+def test_grouped_full_size_sampled(fgq_gpu, name):
+    """Full grouped problem quantised and multiplied on the GPU; for a few
+    experts (the largest, a small one, the last non-empty) sampled rows are
+    checked against the oracle's own quantisation and product."""
+    import torch
+    d = make_workload(name)
+    A, W, off = d["A"], d["W"], d["offsets"]
+    qa, sa = fgq_gpu.quant_act_1x128(dev_bf16(A))
+    qw, sw = fgq_gpu.quant_w_128x128(dev_bf16(W))
+    c = fgq_gpu.grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    counts = d["counts"]
+    nz = np.nonzero(counts)[0]
+    pick = {int(np.argmax(counts)), int(nz[np.argmin(counts[nz])]), int(nz[-1])}
+    rng = np.random.default_rng(3)
+    for e in sorted(pick):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 64)]))
+        qao, sao = oracle.quant_act_1x128(A[rows])
+        qwo, swo = oracle.quant_w_128x128(W[e])
+        ref = oracle.gemm_ref(qao, sao, qwo, swo)
+        _gate(host_bf16_f64(c[rows.tolist()]), ref, f"{name} full, expert {e} ({r1 - r0} rows)")
