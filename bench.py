@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 768 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--mode", default="exact", choices=["exact", "fp8core"],
+                   help="GEMM accumulation: exact products (FP16 matrix cores) or FP8 matrix cores")
     return p.parse_args()
 
 
@@ -138,7 +140,11 @@ def build_sets(args):
     return d, sets, flops, quant_bytes, shape
 
 
-def make_step(args, fgq, d, n_sets):
+def gemm_mode(fgq, name):
+    return fgq.GEMM_EXACT if name == "exact" else fgq.GEMM_FP8_CORE
+
+
+def make_step(args, fgq, d, n_sets, mode):
     """Allocates every output buffer up front; returns step(i, set, timer)
     running the whole path once on input set i."""
     import torch
@@ -173,11 +179,11 @@ def make_step(args, fgq, d, n_sets):
         t.run("quant_w_128x128", lambda: fgq.quant_w_128x128(s["W"], q=o["qw"], s=o["sw"]))
         if args.workload in ("prefill", "decode"):
             t.run("gemm_fp8_blockscaled",
-                  lambda: fgq.gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"]))
+                  lambda: fgq.gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"], mode=mode))
         else:
             t.run("grouped_gemm_fp8_blockscaled",
                   lambda: fgq.grouped_gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], s["off"],
-                                                           out=o["c"]))
+                                                           out=o["c"], mode=mode))
     return step
 
 
@@ -247,7 +253,7 @@ def main():
     torch.cuda.set_device(0)
     print(f"[bench] building {args.workload} inputs", file=sys.stderr, flush=True)
     d, sets, flops, quant_bytes, shape = build_sets(args)
-    step = make_step(args, fgq, d, len(sets))
+    step = make_step(args, fgq, d, len(sets), gemm_mode(fgq, args.mode))
     warm = Timer()
     for i in range(args.warmup):
         step(i % len(sets), sets[i % len(sets)], warm)
@@ -278,6 +284,16 @@ def main():
             kernels[k] = {"ms": ms, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
                           "algorithmic_bytes": quant_bytes[k]}
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    # the other GEMM accumulation mode, timed alone (not part of the step)
+    other = "fp8core" if args.mode == "exact" else "exact"
+    alt_step = make_step(args, fgq, d, len(sets), gemm_mode(fgq, other))
+    alt_t = Timer()
+    for i in range(max(3, args.steps // 2)):
+        alt_step(i % len(sets), sets[i % len(sets)], alt_t)
+    torch.cuda.synchronize()
+    alt_ms = alt_t.avg_ms()[gemm_name]
+    alt = {"mode": other, "ms": alt_ms, "TFLOP/s": flops / (alt_ms * 1e-3) / 1e12,
+           "frac_fp8_peak": flops / (alt_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -301,6 +317,8 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
                      "traffic": traffic_for(gemm_name)},
         "kernels": kernels,
+        "gemm_mode": args.mode,
+        "gemm_other_mode": alt,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
     }

@@ -104,9 +104,10 @@ size_t fgq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                       int64_t sa_skb, const void* qw, int64_t ldw, const float* sw,
                                       int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc, int64_t M,
-                                      int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      int64_t N, int64_t K, int32_t mode, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (mode != FGQ_GEMM_EXACT && mode != FGQ_GEMM_FP8_CORE) return FGQ_ERR_UNSUPPORTED;
   if (N % 128 != 0 || K % 128 != 0 || K == 0) return FGQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return FGQ_OK;
   fgq_status_t st = check_gemm_common(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, N, K);
@@ -120,7 +121,7 @@ fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* 
   }
   return from_hip(fgq::launch_gemm_fp8_blockscaled(
       static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, sw,
-      sw_snb, sw_skb, static_cast<uint16_t*>(c), ldc, M, N, K, workspace, workspace_bytes,
+      sw_snb, sw_skb, static_cast<uint16_t*>(c), ldc, M, N, K, mode, workspace, workspace_bytes,
       as_stream(stream)));
 }
 
@@ -129,8 +130,9 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
                                               const float* sw, int64_t sw_snb, int64_t sw_skb,
                                               int64_t sw_es, const int32_t* offsets, int64_t E,
                                               int64_t total_rows, void* c, int64_t ldc, int64_t N,
-                                              int64_t K, void* stream) {
+                                              int64_t K, int32_t mode, void* stream) {
   if (E < 0 || total_rows < 0 || N < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (mode != FGQ_GEMM_EXACT && mode != FGQ_GEMM_FP8_CORE) return FGQ_ERR_UNSUPPORTED;
   if (N % 128 != 0 || K % 128 != 0 || K == 0) return FGQ_ERR_UNSUPPORTED;
   if (E > 65536 || total_rows >= ((int64_t)1 << 31) - 65536) return FGQ_ERR_UNSUPPORTED;
   if (E == 0 || total_rows == 0 || N == 0) return FGQ_OK;
@@ -142,7 +144,7 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
   if (E > 1 && w_es < N * ldw) return FGQ_ERR_STRIDE;
   return from_hip(fgq::launch_grouped_gemm_fp8_blockscaled(
       static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, w_es,
-      sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, static_cast<uint16_t*>(c), ldc, N, K,
+      sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, static_cast<uint16_t*>(c), ldc, N, K, mode,
       as_stream(stream)));
 }
 
@@ -176,6 +178,13 @@ fgq_status_t fgq_debug_copy(const void* src, void* dst, int64_t bytes, void* str
   if (!src || !dst) return FGQ_ERR_NULL;
   if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0) return FGQ_ERR_ALIGN;
   return from_hip(fgq::launch_debug_copy(src, dst, bytes, as_stream(stream)));
+}
+
+fgq_status_t fgq_debug_mfma_16x16x128(const void* a, const void* b, const float* cin, float* d, void* stream) {
+  if (!a || !b || !cin || !d) return FGQ_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(cin, 4) || !aligned(d, 4)) return FGQ_ERR_ALIGN;
+  return from_hip(fgq::launch_debug_mfma(static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), cin, d,
+                                         as_stream(stream)));
 }
 
 }  // extern "C"

@@ -22,7 +22,7 @@ hipError_t launch_fused_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint
 hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                        int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw,
                                        int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc,
-                                       int64_t M, int64_t N, int64_t K, void* workspace,
+                                       int64_t M, int64_t N, int64_t K, int mode, void* workspace,
                                        size_t workspace_bytes, hipStream_t st);
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -32,10 +32,11 @@ hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, c
                                                int64_t ldw, int64_t w_es, const float* sw,
                                                int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
                                                const int32_t* offsets, int64_t E, int64_t total_rows,
-                                               uint16_t* c, int64_t ldc, int64_t N, int64_t K,
+                                               uint16_t* c, int64_t ldc, int64_t N, int64_t K, int mode,
                                                hipStream_t st);
 
 hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+hipError_t launch_debug_mfma(const uint8_t* a, const uint8_t* b, const float* cin, float* d, hipStream_t st);
 
 }  // namespace fgq

@@ -100,13 +100,15 @@ def test_fused_validation(lib):
 
 
 def gemm(lib, qa=P, lda=256, sa=S, sa_sm=2, sa_skb=1, qw=Q, ldw=256, sw=S, sw_snb=2, sw_skb=1, c=Q,
-         ldc=256, M=4, N=256, K=256, ws=0, ws_bytes=0):
+         ldc=256, M=4, N=256, K=256, mode=0, ws=0, ws_bytes=0):
     return lib.fgq_gemm_fp8_blockscaled(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc,
-                                        M, N, K, ws, ws_bytes, None)
+                                        M, N, K, mode, ws, ws_bytes, None)
 
 
 def test_gemm_validation(lib):
     assert gemm(lib, M=-1) == SHAPE
+    assert gemm(lib, mode=2) == UNSUP
+    assert gemm(lib, mode=-1) == UNSUP
     assert gemm(lib, N=100) == UNSUP
     assert gemm(lib, K=0) == UNSUP
     assert gemm(lib, K=200) == UNSUP
@@ -123,13 +125,14 @@ def test_gemm_validation(lib):
     assert lib.fgq_gemm_workspace_bytes(0, 256, 256) == 0
 
 
-def grouped(lib, E=4, R=100, offsets=S, w_es=256 * 256, N=256, K=256, qa=P, ldc=256):
+def grouped(lib, E=4, R=100, offsets=S, w_es=256 * 256, N=256, K=256, qa=P, ldc=256, mode=0):
     return lib.fgq_grouped_gemm_fp8_blockscaled(qa, 256, S, 2, 1, Q, 256, w_es, S, 2, 1, 4, offsets, E, R,
-                                                Q, ldc, N, K, None)
+                                                Q, ldc, N, K, mode, None)
 
 
 def test_grouped_validation(lib):
     assert grouped(lib, E=-1) == SHAPE
+    assert grouped(lib, mode=7) == UNSUP
     assert grouped(lib, R=-1) == SHAPE
     assert grouped(lib, E=70000) == UNSUP
     assert grouped(lib, K=100) == UNSUP

@@ -2,7 +2,15 @@
 
 Gate (from the workload definition): normwise relative error <= 2e-3 against
 the oracle's float64 result from the same dequantised operands, and
-elementwise <= 1e-2 relative wherever |ref| > 1e-2 * rms(ref).
+elementwise <= 1e-2 relative wherever |ref| > 1e-2 * rms(ref).  The default
+mode (exact products on the FP16 matrix cores) must meet it everywhere.
+
+The FP8-matrix-core mode sums each group of 8 consecutive products in a
+window about 13 bits below the group's largest product (measured on gfx950,
+see tests/test_gpu_mfma_precision.py), so its elementwise check adds that
+window's worst case to the tolerance:
+    |C - C*| <= 1e-2 |C*| + sum_kb |sa sw| * sum_groups 8 * 2**-12 * max_g |a b|
+(the normwise gate is unchanged).
 
   * exact pin: integer-valued codes with power-of-two scales make every
     partial sum exact in binary32, so the GPU result must equal the oracle's
@@ -29,7 +37,45 @@ from tests.gpu_util import Guarded, dev_bf16, dev_f32, dev_u8, host_bf16_f64, lo
 pytestmark = pytest.mark.gpu
 
 
-def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None):
+MODES = [0, 1]   # fgq.GEMM_EXACT, fgq.GEMM_FP8_CORE
+
+
+def fp8_core_slack(qa, sa, qw, sw, rows, cols):
+    """Worst-case truncation of the FP8 matrix core's 8-product groups for the
+    selected outputs (float64): sum over chunks and groups of 8 * 2**-12 times
+    the group's largest |product|, times |sa sw|."""
+    A = oracle.e4m3_decode(qa[rows]).astype(np.float64)
+    W = oracle.e4m3_decode(qw[cols]).astype(np.float64)
+    M, K = A.shape
+    N = W.shape[0]
+    out = np.zeros((M, N))
+    for kb in range(K // 128):
+        a = np.abs(A[:, 128 * kb:128 * kb + 128]).reshape(M, 16, 8)
+        w = np.abs(W[:, 128 * kb:128 * kb + 128]).reshape(N, 16, 8)
+        gmax = np.max(a[:, None, :, :] * w[None, :, :, :], axis=3).sum(axis=2)   # [M, N]
+        scale = np.abs(sa[rows, kb][:, None] * sw[np.asarray(cols) // 128, kb][None, :])
+        out += 8 * 2.0 ** -12 * gmax * scale
+    return out
+
+
+def _check(c, ref, what, mode, qa=None, sa=None, qw=None, sw=None, rows=None):
+    if mode == 0:
+        return _gate(c, ref, what)
+    g = oracle.gemm_gate(c, ref)
+    log(f"{what} [fp8 core]: normwise {g['normwise']:.3e}, max elem {g['max_elem_rel']:.3e}")
+    assert g["finite"] and g["normwise"] <= 2e-3, (what, g)
+    rng = np.random.default_rng(0)
+    M, N = ref.shape
+    rs = np.arange(M) if M <= 64 else np.sort(rng.choice(M, 64, replace=False))
+    cs = np.arange(N) if N <= 512 else np.sort(rng.choice(N, 512, replace=False))
+    src_rows = np.asarray(rows)[rs] if rows is not None else rs
+    slack = fp8_core_slack(qa, sa, qw, sw, src_rows, cs)
+    sub_c, sub_r = c[np.ix_(rs, cs)], ref[np.ix_(rs, cs)]
+    assert np.all(np.abs(sub_c - sub_r) <= 1e-2 * np.abs(sub_r) + slack), what
+    return g
+
+
+def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None, mode=0):
     import torch
     M, K = qa.shape
     N = qw.shape[0]
@@ -40,7 +86,7 @@ def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None):
     else:
         qa_d = dev_u8(qa)
     cg = Guarded(M, N, torch.bfloat16, ld=ldc)
-    fgq.gemm_fp8_blockscaled(qa_d, dev_f32(sa), dev_u8(qw), dev_f32(sw), out=cg.view)
+    fgq.gemm_fp8_blockscaled(qa_d, dev_f32(sa), dev_u8(qw), dev_f32(sw), out=cg.view, mode=mode)
     torch.cuda.synchronize()
     cg.check_canaries()
     return host_bf16_f64(cg.view)
@@ -65,18 +111,20 @@ def _int_codes(shape, rng):
     return lut[ints + 8]
 
 
-def test_gemm_integer_codes_bit_exact(fgq_gpu):
+@pytest.mark.parametrize("mode", MODES)
+def test_gemm_integer_codes_bit_exact(fgq_gpu, mode):
     rng = np.random.default_rng(0)
     M, N, K = 200, 384, 7168
     qa, qw = _int_codes((M, K), rng), _int_codes((N, K), rng)
     sa = (2.0 ** rng.integers(-1, 2, (M, K // 128))).astype(np.float32)
     sw = (2.0 ** rng.integers(-1, 2, (N // 128, K // 128))).astype(np.float32)
     ref = oracle.gemm_ref(qa, sa, qw, sw)
-    c = _gemm(fgq_gpu, qa, sa, qw, sw)
+    c = _gemm(fgq_gpu, qa, sa, qw, sw, mode=mode)
     assert np.array_equal(c, oracle.bf16_round_f64(ref))
 
 
-def test_gemm_one_hot_scale_indexing(fgq_gpu):
+@pytest.mark.parametrize("mode", MODES)
+def test_gemm_one_hot_scale_indexing(fgq_gpu, mode):
     rng = np.random.default_rng(1)
     M, N, K = 150, 512, 1024
     qa = np.zeros((M, K), np.uint8)
@@ -86,32 +134,35 @@ def test_gemm_one_hot_scale_indexing(fgq_gpu):
     sa = rng.uniform(0.5, 2, (M, K // 128)).astype(np.float32)
     sw = rng.uniform(0.5, 2, (N // 128, K // 128)).astype(np.float32)
     ref = oracle.gemm_ref(qa, sa, qw, sw)
-    c = _gemm(fgq_gpu, qa, sa, qw, sw)
+    c = _gemm(fgq_gpu, qa, sa, qw, sw, mode=mode)
     # one product per output: exact up to the rounding of sa*sw and the BF16 output
     assert np.all(np.abs(c - ref) <= np.abs(ref) * (2.0 ** -8 + 2.0 ** -22))
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("M,N,K,lda,ldc", [(1, 128, 128, None, None), (129, 256, 384, None, None),
                                            (300, 384, 1024, 1040, 392), (64, 128, 7168, None, None),
-                                           (255, 640, 2048, None, 648)])
-def test_gemm_shapes_oracle_operands(fgq_gpu, M, N, K, lda, ldc):
+                                           (255, 640, 2048, None, 648), (513, 768, 512, None, None),
+                                           (256, 256, 256, None, None)])
+def test_gemm_shapes_oracle_operands(fgq_gpu, M, N, K, lda, ldc, mode):
     a = normal_bf16((M, K), 1.0, rng_for(5, M))
     w = normal_bf16((N, K), 0.02, rng_for(5, N + 1))
     qa, sa = oracle.quant_act_1x128(a)
     qw, sw = oracle.quant_w_128x128(w)
     ref = oracle.gemm_ref(qa, sa, qw, sw)
-    c = _gemm(fgq_gpu, qa, sa, qw, sw, ldc=ldc, lda=lda)
-    _gate(c, ref, f"gemm {M}x{N}x{K}")
+    c = _gemm(fgq_gpu, qa, sa, qw, sw, ldc=ldc, lda=lda, mode=mode)
+    _check(c, ref, f"gemm {M}x{N}x{K}", mode, qa, sa, qw, sw)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name,rows", [("tiny", None), ("decode", None), ("prefill", 384)])
-def test_gemm_workloads_oracle_operands(fgq_gpu, name, rows):
+def test_gemm_workloads_oracle_operands(fgq_gpu, name, rows, mode):
     d = make_workload(name, rows=rows)
     qa, sa = oracle.quant_act_1x128(d["A"])
     qw, sw = oracle.quant_w_128x128(d["W"])
     ref = oracle.gemm_ref(qa, sa, qw, sw)
-    c = _gemm(fgq_gpu, qa, sa, qw, sw)
-    _gate(c, ref, f"gemm {name}")
+    c = _gemm(fgq_gpu, qa, sa, qw, sw, mode=mode)
+    _check(c, ref, f"gemm {name}", mode, qa, sa, qw, sw)
     # reported, not gated: distance to the unquantised BF16 product
     a64 = oracle.f32_from_bf16(d["A"]).astype(np.float64)
     w64 = oracle.f32_from_bf16(d["W"]).astype(np.float64)
@@ -119,7 +170,8 @@ def test_gemm_workloads_oracle_operands(fgq_gpu, name, rows):
     log(f"  vs unquantised BF16 operands: normwise {np.linalg.norm(c - exact) / np.linalg.norm(exact):.3e}")
 
 
-def test_gemm_prefill_full_size_sampled(fgq_gpu):
+@pytest.mark.parametrize("mode", MODES)
+def test_gemm_prefill_full_size_sampled(fgq_gpu, mode):
     """8192x7168x18432 end to end on the GPU (quantise A and W, GEMM) as the
     benchmark runs it; 192 sampled rows against the oracle's own
     quantisation and float64 product."""
@@ -128,33 +180,35 @@ def test_gemm_prefill_full_size_sampled(fgq_gpu):
     A, W = d["A"], d["W"]
     qa, sa = fgq_gpu.quant_act_1x128(dev_bf16(A))
     qw, sw = fgq_gpu.quant_w_128x128(dev_bf16(W))
-    c = fgq_gpu.gemm_fp8_blockscaled(qa, sa, qw, sw)
+    c = fgq_gpu.gemm_fp8_blockscaled(qa, sa, qw, sw, mode=mode)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(2).choice(A.shape[0], 192, replace=False))
     rows[0], rows[-1] = 0, A.shape[0] - 1
     qao, sao = oracle.quant_act_1x128(A[rows])
     qwo, swo = oracle.quant_w_128x128(W)
     ref = oracle.gemm_ref(qao, sao, qwo, swo)
-    _gate(host_bf16_f64(c[rows.tolist()]), ref, "prefill full (sampled rows)")
+    _check(host_bf16_f64(c[rows.tolist()]), ref, "prefill full (sampled rows)", mode, qao, sao, qwo, swo)
 
 
 # ------------------------------------------------------------------ grouped
 
-def _grouped(fgq, qa, sa, qw, sw, offsets):
+def _grouped(fgq, qa, sa, qw, sw, offsets, mode=0):
     import torch
     R = qa.shape[0]
     N = qw.shape[1]
     cg = Guarded(R, N, torch.bfloat16)
     fgq.grouped_gemm_fp8_blockscaled(dev_u8(qa), dev_f32(sa), dev_u8(qw), dev_f32(sw),
-                                     torch.from_numpy(np.asarray(offsets, np.int32)).cuda(), out=cg.view)
+                                     torch.from_numpy(np.asarray(offsets, np.int32)).cuda(), out=cg.view,
+                                     mode=mode)
     torch.cuda.synchronize()
     cg.check_canaries()
     return host_bf16_f64(cg.view)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("counts", [[0, 200, 0, 57], [300, 0, 0, 0], [1, 1, 1, 130], [0, 0, 0, 5],
-                                    [129, 127, 128, 256]])
-def test_grouped_ragged_counts(fgq_gpu, counts):
+                                    [129, 127, 128, 256], [0, 700, 1, 0, 256, 255]])
+def test_grouped_ragged_counts(fgq_gpu, counts, mode):
     E, N, K = len(counts), 256, 512
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(off[-1])
@@ -163,33 +217,57 @@ def test_grouped_ragged_counts(fgq_gpu, counts):
     qa, sa = oracle.quant_act_1x128(a)
     qw, sw = oracle.quant_w_128x128(w)
     ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
-    c = _grouped(fgq_gpu, qa, sa, qw, sw, off)
-    _gate(c, ref, f"grouped {counts}")
+    c = _grouped(fgq_gpu, qa, sa, qw, sw, off, mode=mode)
+    if mode == 0:
+        _gate(c, ref, f"grouped {counts}")
+    else:
+        _check_grouped_fp8(c, ref, qa, sa, qw, sw, off, f"grouped {counts}")
 
 
-def test_grouped_single_expert_equals_dense(fgq_gpu):
+def _check_grouped_fp8(c, ref, qa, sa, qw, sw, off, what):
+    g = oracle.gemm_gate(c, ref)
+    log(f"{what} [fp8 core]: normwise {g['normwise']:.3e}, max elem {g['max_elem_rel']:.3e}")
+    assert g["finite"] and g["normwise"] <= 2e-3, (what, g)
+    for e in range(len(off) - 1):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            rows = np.arange(r0, min(r1, r0 + 32))
+            cols = np.arange(min(qw.shape[1], 256))
+            slack = fp8_core_slack(qa, sa, qw[e], sw[e], rows, cols)
+            sub_c, sub_r = c[np.ix_(rows, cols)], ref[np.ix_(rows, cols)]
+            assert np.all(np.abs(sub_c - sub_r) <= 1e-2 * np.abs(sub_r) + slack), (what, e)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_grouped_single_expert_equals_dense(fgq_gpu, mode):
     M, N, K = 333, 384, 1024
     a = normal_bf16((M, K), 1.0, rng_for(7, 1))
     w = normal_bf16((1, N, K), 0.02, rng_for(7, 2))
     qa, sa = oracle.quant_act_1x128(a)
     qw, sw = oracle.quant_w_128x128(w)
-    g = _grouped(fgq_gpu, qa, sa, qw, sw, [0, M])
-    d = _gemm(fgq_gpu, qa, sa, qw[0], sw[0])
+    g = _grouped(fgq_gpu, qa, sa, qw, sw, [0, M], mode=mode)
+    d = _gemm(fgq_gpu, qa, sa, qw[0], sw[0], mode=mode)
     assert np.array_equal(g, d)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name", ["grouped_up", "fused_down"])
-def test_grouped_workloads_reduced_rows(fgq_gpu, name):
+def test_grouped_workloads_reduced_rows(fgq_gpu, name, mode):
     d = make_workload(name, rows=1500)
     qa, sa = oracle.quant_act_1x128(d["A"])
     qw, sw = oracle.quant_w_128x128(d["W"])
     ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, d["offsets"])
-    c = _grouped(fgq_gpu, qa, sa, qw, sw, d["offsets"])
-    _gate(c, ref, f"{name} rows={d['R']} counts={d['counts'].tolist()}")
+    c = _grouped(fgq_gpu, qa, sa, qw, sw, d["offsets"], mode=mode)
+    what = f"{name} rows={d['R']} counts={d['counts'].tolist()}"
+    if mode == 0:
+        _gate(c, ref, what)
+    else:
+        _check_grouped_fp8(c, ref, qa, sa, qw, sw, d["offsets"], what)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name", ["grouped_up", "fused_down"])
-def test_grouped_full_size_sampled(fgq_gpu, name):
+def test_grouped_full_size_sampled(fgq_gpu, name, mode):
     """Full grouped problem quantised and multiplied on the GPU; for a few
     experts (the largest, a small one, the last non-empty) sampled rows are
     checked against the oracle's own quantisation and product."""
@@ -198,7 +276,7 @@ def test_grouped_full_size_sampled(fgq_gpu, name):
     A, W, off = d["A"], d["W"], d["offsets"]
     qa, sa = fgq_gpu.quant_act_1x128(dev_bf16(A))
     qw, sw = fgq_gpu.quant_w_128x128(dev_bf16(W))
-    c = fgq_gpu.grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda())
+    c = fgq_gpu.grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda(), mode=mode)
     torch.cuda.synchronize()
     counts = d["counts"]
     nz = np.nonzero(counts)[0]
@@ -210,4 +288,5 @@ def test_grouped_full_size_sampled(fgq_gpu, name):
         qao, sao = oracle.quant_act_1x128(A[rows])
         qwo, swo = oracle.quant_w_128x128(W[e])
         ref = oracle.gemm_ref(qao, sao, qwo, swo)
-        _gate(host_bf16_f64(c[rows.tolist()]), ref, f"{name} full, expert {e} ({r1 - r0} rows)")
+        _check(host_bf16_f64(c[rows.tolist()]), ref, f"{name} full, expert {e} ({r1 - r0} rows)", mode,
+               qao, sao, qwo, swo)
