@@ -159,6 +159,8 @@ def make_step(args, fgq, d, n_sets, mode):
             o["qw"] = torch.empty((N, K), dtype=torch.uint8, device="cuda")
             o["sw"] = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
             o["c"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ws = fgq.gemm_workspace_bytes(M, N, K)
+            o["ws"] = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda") if ws else None
         else:
             R, K, N, E = d["R"], d["K"], d["N"], d["E"]
             if args.workload == "fused_down":
@@ -179,7 +181,8 @@ def make_step(args, fgq, d, n_sets, mode):
         t.run("quant_w_128x128", lambda: fgq.quant_w_128x128(s["W"], q=o["qw"], s=o["sw"]))
         if args.workload in ("prefill", "decode"):
             t.run("gemm_fp8_blockscaled",
-                  lambda: fgq.gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"], mode=mode))
+                  lambda: fgq.gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"],
+                                                   workspace=o["ws"], mode=mode))
         else:
             t.run("grouped_gemm_fp8_blockscaled",
                   lambda: fgq.grouped_gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], s["off"],

@@ -22,6 +22,14 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte streaming store (non-temporal hint: the codes are not re-read here).
+__device__ __forceinline__ void store_nt8(void* p, uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+
 // clamp(y, -448, 448); v_med3_f32 returns y itself (sign of zero included)
 // whenever y is inside the interval.
 __device__ __forceinline__ float clamp448(float y) {

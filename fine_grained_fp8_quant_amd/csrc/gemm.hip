@@ -26,8 +26,8 @@
 //     layout, so whatever order the unit pairs the 128 K positions in, the
 //     sum is the full chunk dot product.
 //   * LDS rows are 128 bytes (one chunk); the 16-byte column c of row r is
-//     stored at column c ^ (r & 7) so that 16 lanes reading 16 different
-//     rows at one logical column hit different banks.
+//     stored at column c ^ ((r / 2) mod 8) so that 16 lanes reading 16
+//     consecutive rows at one logical column hit all 64 banks once.
 //   * Global -> register -> LDS double buffering: chunk kb+1 is in flight
 //     while chunk kb is multiplied.
 #include "fgq_device.h"
@@ -75,12 +75,20 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
 __device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 4, 0, 0);
 }
-// wait for this wave's outstanding global loads (LDS DMA included)
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediate: at most n of this wave's vector memory operations (LDS
+// DMA included) outstanding and every LDS operation finished (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at 7, lgkmcnt 11:8 = 0).
+constexpr int waitcnt_vm_lds(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+// Workgroup barrier without the implicit wait for all outstanding global
+// loads that __syncthreads() adds (it would drain the DMA pipeline).  LDS
+// visibility is the caller's job (waitcnt before it); the memory clobber
+// keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void barrier_no_drain() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_ = 2>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NSTAGE = NSTAGE_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
@@ -88,10 +96,15 @@ struct TileCfg {
   static constexpr int NBW = BN >= 128 ? BN / 128 : 1;  // weight-scale blocks per tile
   static constexpr int SA_OFF = A_BYTES + B_BYTES;
   static constexpr int SW_OFF = SA_OFF + BM * 4;
-  static constexpr int STAGE = SW_OFF + 256;
+  static constexpr int STAGE = SW_OFF + 256;   // weight scales, then a dummy slot at +128
   static constexpr int A_INS = BM / 8, B_INS = BN / 8;       // 1 KB DMA instructions per stage
   static constexpr int A_PER_W = (A_INS + NW - 1) / NW, B_PER_W = (B_INS + NW - 1) / NW;
   static constexpr int SA_INS = (BM + 63) / 64;
+  // every wave issues the same DMA instructions per chunk: its A and B
+  // slices and one 4-byte load (activation scales, weight scales, or a dummy)
+  static constexpr int DMA_PER_CHUNK = A_PER_W + B_PER_W + 1;
+  static_assert(A_INS % NW == 0 && B_INS % NW == 0, "uniform DMA count per wave");
+  static_assert(NSTAGE >= 2 && (NSTAGE - 2) * DMA_PER_CHUNK <= 63, "vmcnt range");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile is a multiple of 16x16");
   static_assert(BM % 8 == 0 && BN % 8 == 0, "whole DMA instructions");
   static_assert(WN <= 128 && (128 % WN == 0), "a wave's columns share one weight-scale block");
@@ -99,27 +112,39 @@ struct TileCfg {
   static_assert(NBW <= 64, "weight scales fit one instruction");
 };
 
-// One output tile [row_begin, row_begin + BM) x [n0, n0 + BN); rows >= row_end
-// are neither read (their loads repeat row row_end - 1) nor written.
-template <class C, int MODE>
+// Physical 16-byte column of logical column c in LDS row r.  A fragment read
+// has 16 lanes on 16 consecutive rows at one logical column; rows are 128
+// bytes (32 of the 64 four-byte banks), so rows r and r + 2 share banks
+// unless their columns differ: XOR with (r / 2) mod 8 spreads the 16 rows
+// over all 64 banks.
+__device__ __forceinline__ int lds_col(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// One output tile [row_begin, row_begin + BM) x [n0, n0 + BN) over the K
+// chunks [kb_begin, kb_end); rows >= row_end are neither read (their loads
+// repeat row row_end - 1) nor written.  Writes BF16 C, or with PARTIAL the
+// binary32 sums of its chunks to part[m * ldc + n] (split-K workspace).
+template <class C, int MODE, bool PARTIAL = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_t lda,
                                           const float* __restrict__ sa, int64_t sa_sm, int64_t sa_skb,
                                           int64_t row_begin, int64_t row_end,
                                           const uint8_t* __restrict__ qw, int64_t ldw,
                                           const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
-                                          int64_t n0, uint16_t* __restrict__ c, int64_t ldc, int KB,
-                                          uint8_t* lds) {
+                                          int64_t n0, uint16_t* __restrict__ c, float* __restrict__ part,
+                                          int64_t ldc, int kb_begin, int kb_end, uint8_t* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int l16 = lane & 15, lgrp = lane >> 4;
 
-  // ---- this lane's DMA sources: slot s = ins * 64 + lane holds row s / 8,
-  // physical column s % 8 = logical column (s % 8) ^ (row & 7).  Rows of one
-  // lane differ by multiples of 8 * NW, so (row & 7) = (lane / 8) & 7 for all
-  // of them; sources are the tile base plus 32-bit offsets.
-  const int dcol = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;
+  // ---- this lane's DMA sources: slot s = ins * 64 + lane holds row s / 8 at
+  // physical column s % 8, i.e. the logical column whose lds_col is s % 8
+  // (the XOR is its own inverse).  Row = 8 * ins + lane / 8 with ins = wave +
+  // j * NW (NW even), so row & 15 = 8 * (wave & 1) + lane / 8 for every j and
+  // one column offset serves all of them; sources are the tile base plus
+  // 32-bit offsets.
+  static_assert(C::NW % 2 == 0, "instruction parity follows the wave's");
+  const int dcol = lds_col(lane & 7, ((wave & 1) << 3) | (lane >> 3)) * 16;
   const uint8_t* a_tile = qa + row_begin * lda;
   const int64_t a_last = row_end - 1 - row_begin;
   uint32_t a_src[C::A_PER_W];
@@ -149,19 +174,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
     const uint8_t* at = a_tile + (int64_t)kb * 128;
     const uint8_t* bt = b_tile + (int64_t)kb * 128;
 #pragma unroll
-    for (int j = 0; j < C::A_PER_W; ++j) {
-      const int ins = wave + j * C::NW;
-      if (C::A_INS % C::NW == 0 || ins < C::A_INS) dma16(at + a_src[j], base + ins * 1024);
-    }
+    for (int j = 0; j < C::A_PER_W; ++j) dma16(at + a_src[j], base + (wave + j * C::NW) * 1024);
 #pragma unroll
-    for (int j = 0; j < C::B_PER_W; ++j) {
-      const int ins = wave + j * C::NW;
-      if (C::B_INS % C::NW == 0 || ins < C::B_INS) dma16(bt + b_src[j], base + C::A_BYTES + ins * 1024);
-    }
+    for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
     if (wave < C::SA_INS) {
       dma4(s_src + (int64_t)kb * sa_skb, base + C::SA_OFF + wave * 256);
-    } else if (wave == C::SA_INS && lane < C::NBW) {
-      dma4(s_src + (int64_t)kb * sw_skb, base + C::SW_OFF);
+    } else if (wave == C::SA_INS) {
+      if (lane < C::NBW) dma4(s_src + (int64_t)kb * sw_skb, base + C::SW_OFF);
+    } else if (lane == 0) {
+      dma4(sw, base + C::SW_OFF + 128);  // dummy: keeps the per-wave DMA count uniform
     }
   };
 
@@ -173,21 +194,31 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
 
   // LDS byte offsets of this lane's fragment rows: 32 contiguous code bytes
   // (logical columns 2*lgrp, 2*lgrp + 1 of the 128-byte chunk row).  Sub-tile
-  // rows step by 16, which keeps (row & 7), so sub-tiles are base + 2048 * i.
-  const int c0 = lgrp * 2, rsw = l16 & 7;
-  const int a_off0 = (wm * C::WM + l16) * 128 + ((c0 ^ rsw) << 4);
-  const int a_off1 = (wm * C::WM + l16) * 128 + (((c0 + 1) ^ rsw) << 4);
-  const int b_off0 = C::A_BYTES + (wn * C::WN + l16) * 128 + ((c0 ^ rsw) << 4);
-  const int b_off1 = C::A_BYTES + (wn * C::WN + l16) * 128 + (((c0 + 1) ^ rsw) << 4);
+  // rows step by 16, which keeps row & 15, so sub-tiles are base + 2048 * i.
+  // Wave tile origins are multiples of 16 rows as well.
+  const int c0 = lgrp * 2;
+  const int a_off0 = (wm * C::WM + l16) * 128 + (lds_col(c0, l16) << 4);
+  const int a_off1 = (wm * C::WM + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
+  const int b_off0 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0, l16) << 4);
+  const int b_off1 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
   const int sa_off = C::SA_OFF + (wm * C::WM + lgrp * 4) * 4;
   const int sw_idx = (wn * C::WN) / 128;
 
-  issue(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
-    const uint8_t* base = lds + (kb & 1) * C::STAGE;
+  // NSTAGE-deep pipeline: chunk kb + NSTAGE - 1 is requested while chunk kb
+  // is multiplied.  At the top of iteration kb, the wait leaves the chunks
+  // issued after kb in flight; the barrier then publishes chunk kb to every
+  // wave and frees the stage of chunk kb - 1, which the next request reuses.
+#pragma unroll
+  for (int p = 0; p < C::NSTAGE - 1; ++p)
+    if (kb_begin + p < kb_end) issue(kb_begin + p, p);
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const int it = kb - kb_begin;
+    const int stage = it % C::NSTAGE;
+    if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
+    barrier_no_drain();
+    if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
+    const uint8_t* base = lds + stage * C::STAGE;
     const float swv = reinterpret_cast<const float*>(base + C::SW_OFF)[sw_idx];
     if constexpr (MODE == 1) {
       // FP8 matrix core: one instruction per 16x16 sub-tile and chunk
@@ -198,12 +229,20 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
         const uint4 hi = *reinterpret_cast<const uint4*>(base + b_off1 + ni * 2048);
         bf[ni] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
+      // A codes and scales one sub-tile row ahead
+      uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
+      uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
+      v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
 #pragma unroll
       for (int mi = 0; mi < C::TM; ++mi) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + a_off0 + mi * 2048);
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + a_off1 + mi * 2048);
-        const v8i af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off + mi * 64);
+        uint4 nlo = alo, nhi = ahi;
+        v4f nsa = sa4;
+        if (mi + 1 < C::TM) {
+          nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+          nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+          nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
+        }
+        const v8i af = (v8i){(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
         const float s0 = sa4[0] * swv, s1 = sa4[1] * swv, s2 = sa4[2] * swv, s3 = sa4[3] * swv;
 #pragma unroll
         for (int ni = 0; ni < C::TN; ++ni) {
@@ -213,6 +252,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
           acc[mi][ni][2] = __builtin_fmaf(t[2], s2, acc[mi][ni][2]);
           acc[mi][ni][3] = __builtin_fmaf(t[3], s3, acc[mi][ni][3]);
         }
+        alo = nlo;
+        ahi = nhi;
+        sa4 = nsa;
       }
     } else {
       // exact products: codes -> FP16 in registers, four K = 32 steps per chunk
@@ -226,33 +268,42 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
         bh[ni][2] = e4m3x8_to_f16(hi.x, hi.y);
         bh[ni][3] = e4m3x8_to_f16(hi.z, hi.w);
       }
+      uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
+      uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
+      v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
 #pragma unroll
       for (int mi = 0; mi < C::TM; ++mi) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + a_off0 + mi * 2048);
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + a_off1 + mi * 2048);
-        v8h ah[4];
-        ah[0] = e4m3x8_to_f16(lo.x, lo.y);
-        ah[1] = e4m3x8_to_f16(lo.z, lo.w);
-        ah[2] = e4m3x8_to_f16(hi.x, hi.y);
-        ah[3] = e4m3x8_to_f16(hi.z, hi.w);
-        const v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off + mi * 64);
+        uint4 nlo = alo, nhi = ahi;
+        v4f nsa = sa4;
+        if (mi + 1 < C::TM) {
+          nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+          nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+          nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
+        }
+        const uint32_t aw[8] = {alo.x, alo.y, alo.z, alo.w, ahi.x, ahi.y, ahi.z, ahi.w};
+        // K step ks: convert 8 codes of A, then one MFMA into each of the TN
+        // independent sub-tile chains
+        v4f t[C::TN];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const v8h a = e4m3x8_to_f16(aw[2 * ks], aw[2 * ks + 1]);
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni)
+            t[ni] = mfma_16x16x32_f16(a, bh[ni][ks], ks == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : t[ni]);
+        }
         const float s0 = sa4[0] * swv, s1 = sa4[1] * swv, s2 = sa4[2] * swv, s3 = sa4[3] * swv;
 #pragma unroll
         for (int ni = 0; ni < C::TN; ++ni) {
-          // one chunk of one sub-tile: four chained K = 32 steps, then promote
-          v4f t = mfma_16x16x32_f16(ah[0], bh[ni][0], (v4f){0.0f, 0.0f, 0.0f, 0.0f});
-          t = mfma_16x16x32_f16(ah[1], bh[ni][1], t);
-          t = mfma_16x16x32_f16(ah[2], bh[ni][2], t);
-          t = mfma_16x16x32_f16(ah[3], bh[ni][3], t);
-          acc[mi][ni][0] = __builtin_fmaf(t[0], s0, acc[mi][ni][0]);
-          acc[mi][ni][1] = __builtin_fmaf(t[1], s1, acc[mi][ni][1]);
-          acc[mi][ni][2] = __builtin_fmaf(t[2], s2, acc[mi][ni][2]);
-          acc[mi][ni][3] = __builtin_fmaf(t[3], s3, acc[mi][ni][3]);
+          acc[mi][ni][0] = __builtin_fmaf(t[ni][0], s0, acc[mi][ni][0]);
+          acc[mi][ni][1] = __builtin_fmaf(t[ni][1], s1, acc[mi][ni][1]);
+          acc[mi][ni][2] = __builtin_fmaf(t[ni][2], s2, acc[mi][ni][2]);
+          acc[mi][ni][3] = __builtin_fmaf(t[ni][3], s3, acc[mi][ni][3]);
         }
+        alo = nlo;
+        ahi = nhi;
+        sa4 = nsa;
       }
     }
-    wait_vmem();
-    __syncthreads();
   }
 
   // epilogue: lane holds rows lgrp*4 + i, column l16 of each 16x16 sub-tile
@@ -262,9 +313,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
     for (int i = 0; i < 4; ++i) {
       const int64_t gr = row_begin + wm * C::WM + mi * 16 + lgrp * 4 + i;
       if (gr < row_end) {
-        uint16_t* crow = c + gr * ldc + n0 + wn * C::WN + l16;
+        if constexpr (PARTIAL) {
+          float* prow = part + gr * ldc + n0 + wn * C::WN + l16;
 #pragma unroll
-        for (int ni = 0; ni < C::TN; ++ni) crow[ni * 16] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+          for (int ni = 0; ni < C::TN; ++ni) prow[ni * 16] = acc[mi][ni][i];
+        } else {
+          uint16_t* crow = c + gr * ldc + n0 + wn * C::WN + l16;
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) crow[ni * 16] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+        }
       }
     }
   }
@@ -288,8 +345,10 @@ __device__ __forceinline__ void tile_of(int bid, int G, int tiles_m, int& tm, in
   tn = in / gm;
 }
 
-using BigCfg = TileCfg<256, 256, 2, 4>;
+using BigCfg = TileCfg<256, 256, 2, 4>;      // FP8 matrix core, large M
+using BigExactCfg = TileCfg<192, 256, 2, 4>; // exact products, large M (FP16 operands need more registers)
 using SmallCfg = TileCfg<64, 128, 1, 4>;
+using SplitCfg = TileCfg<64, 64, 1, 4, 4>;   // split-K, memory-bound small M: 4-deep prefetch, 2 per CU
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict__ qa, int64_t lda,
@@ -299,14 +358,82 @@ __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict
                                                        int64_t sw_snb, int64_t sw_skb,
                                                        uint16_t* __restrict__ c, int64_t ldc, int64_t M,
                                                        int tiles_m, int KB) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tm, tn);
   gemm_tile<C, MODE>(qa, lda, sa, sa_sm, sa_skb, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
-                     (int64_t)tn * C::BN, c, ldc, KB, lds);
+                     (int64_t)tn * C::BN, c, nullptr, ldc, 0, KB, lds);
 }
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+// Split-K for small M (memory-bound shapes): workgroup (tile, split) sums
+// chunks [split * KB / S, (split + 1) * KB / S) into part[split][M][N].
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs_splitk(const uint8_t* __restrict__ qa, int64_t lda,
+                                                              const float* __restrict__ sa, int64_t sa_sm,
+                                                              int64_t sa_skb, const uint8_t* __restrict__ qw,
+                                                              int64_t ldw, const float* __restrict__ sw,
+                                                              int64_t sw_snb, int64_t sw_skb,
+                                                              float* __restrict__ part, int64_t M, int64_t N,
+                                                              int tiles_m, int tiles, int KB, int S) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
+  const int split = blockIdx.x / tiles;
+  int tm, tn;
+  tile_of(blockIdx.x % tiles, tiles, tiles_m, tm, tn);
+  const int kb0 = (int)((int64_t)split * KB / S), kb1 = (int)((int64_t)(split + 1) * KB / S);
+  gemm_tile<C, MODE, true>(qa, lda, sa, sa_sm, sa_skb, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
+                           (int64_t)tn * C::BN, nullptr, part + (int64_t)split * M * N, N, kb0, kb1, lds);
+}
+
+// C[m, n] = bf16(sum over splits s = 0, 1, ... of part[s][m][n]), in split
+// order (deterministic).  Eight consecutive outputs per thread.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S, int64_t M,
+                                                       int64_t N, uint16_t* __restrict__ c, int64_t ldc) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= M * N) return;
+  const int64_t m = i / N, n = i - m * N;
+  float v[8];
+  const float4* p = reinterpret_cast<const float4*>(part + i);
+  float4 x = p[0], y = p[1];
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  for (int s = 1; s < S; ++s) {
+    p = reinterpret_cast<const float4*>(part + (int64_t)s * M * N + i);
+    x = p[0];
+    y = p[1];
+    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w; v[4] += y.x; v[5] += y.y; v[6] += y.z; v[7] += y.w;
+  }
+  uint4 o;
+  o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+  o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+  o.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+  o.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  *reinterpret_cast<uint4*>(c + m * ldc + n) = o;
+}
+
+// Split-K plan for a dense shape: S > 1 when M is small enough that the
+// output tiles alone cannot fill the 256 compute units several times over.
+// The same function decides the workspace size and the launch.
+struct SplitPlan {
+  int S;
+  int tiles_m, tiles_n;
+};
+static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+  SplitPlan p{1, 0, 0};
+  if (M > 128 || N % SplitCfg::BN != 0) return p;
+  p.tiles_m = (int)((M + SplitCfg::BM - 1) / SplitCfg::BM);
+  p.tiles_n = (int)(N / SplitCfg::BN);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  const int KB = (int)(K / 128);
+  int S = (int)((1024 + tiles - 1) / tiles);  // aim at >= 1024 workgroups (two per CU at a time)
+  if (S > KB / 4) S = KB / 4;                 // at least 4 chunks per split
+  if (S > 16) S = 16;
+  p.S = S < 2 ? 1 : S;
+  return p;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const SplitPlan p = split_plan(M, N, K);
+  return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
 
 template <class C, int MODE>
 static void launch_dense(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm, int64_t sa_skb,
@@ -318,17 +445,35 @@ static void launch_dense(const uint8_t* qa, int64_t lda, const float* sa, int64_
                      sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, tiles_m, (int)(K / 128));
 }
 
+template <int MODE>
+static void launch_splitk(const SplitPlan& p, const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                          int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw, int64_t sw_snb,
+                          int64_t sw_skb, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                          float* part, hipStream_t st) {
+  using C = SplitCfg;
+  const int tiles = p.tiles_m * p.tiles_n;
+  hipLaunchKernelGGL((k_gemm_fp8_bs_splitk<C, MODE>), dim3(tiles * p.S), dim3(C::NT), 0, st, qa, lda, sa, sa_sm,
+                     sa_skb, qw, ldw, sw, sw_snb, sw_skb, part, M, N, p.tiles_m, tiles, (int)(K / 128), p.S);
+  const int64_t groups = (M * N + 7) / 8;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, part, p.S, M, N,
+                     c, ldc);
+}
+
 hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                        int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw,
                                        int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc,
-                                       int64_t M, int64_t N, int64_t K, int mode, void*, size_t,
+                                       int64_t M, int64_t N, int64_t K, int mode, void* workspace, size_t,
                                        hipStream_t st) {
+  const SplitPlan p = split_plan(M, N, K);
+  float* part = static_cast<float*>(workspace);
   const bool big = M > 128 && N % 256 == 0;
   if (mode == 1) {
-    if (big) launch_dense<BigCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+    if (p.S > 1) launch_splitk<1>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
+    else if (big) launch_dense<BigCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
     else launch_dense<SmallCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
   } else {
-    if (big) launch_dense<BigCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+    if (p.S > 1) launch_splitk<0>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
+    else if (big) launch_dense<BigExactCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
     else launch_dense<SmallCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
   }
   return hipGetLastError();
@@ -347,7 +492,7 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
     const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
     const int32_t* __restrict__ offsets, int E, int64_t total_rows, uint16_t* __restrict__ c,
     int64_t ldc, int slots, int KB) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
   int* scan = reinterpret_cast<int*>(lds);  // reused before the tile loop starts
   __shared__ int found[3];
   const int tid = threadIdx.x;
@@ -390,7 +535,7 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
   if (e < 0) return;  // slot past the last tile: the whole workgroup leaves
   const int64_t row_begin = found[1], row_end = found[2];
   gemm_tile<C, MODE>(qa, lda, sa, sa_sm, sa_skb, row_begin, row_end, qw + (int64_t)e * w_es, ldw,
-                     sw + (int64_t)e * sw_es, sw_snb, sw_skb, (int64_t)tn * C::BN, c, ldc, KB, lds);
+                     sw + (int64_t)e * sw_es, sw_snb, sw_skb, (int64_t)tn * C::BN, c, nullptr, ldc, 0, KB, lds);
 }
 
 template <class C, int MODE>
@@ -419,7 +564,7 @@ hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, c
     if (big) launch_grouped<BigCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
     else launch_grouped<SmallCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
   } else {
-    if (big) launch_grouped<BigCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
+    if (big) launch_grouped<BigExactCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
     else launch_grouped<SmallCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
   }
   return hipGetLastError();

@@ -55,8 +55,7 @@ __global__ __launch_bounds__(256) void k_quant_act_1x128(
     const float a = max16(absmax8(f));
     float sc, r;
     group_scales(a, sc, r);
-    const uint2 o = cast8(f, r);
-    *reinterpret_cast<uint2*>(q + (int64_t)mm[u] * ldq + kk[u] * 128u + lane16 * 8u) = o;
+    store_nt8(q + (int64_t)mm[u] * ldq + kk[u] * 128u + lane16 * 8u, cast8(f, r));
     if (lane16 == 0) s[(int64_t)mm[u] * s_sm + (int64_t)kk[u] * s_skb] = sc;
   }
 }

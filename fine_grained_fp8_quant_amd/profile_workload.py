@@ -1,0 +1,53 @@
+"""A short, fixed run of the hot path for hardware-counter profiling:
+
+    rocprofv3 --pmc <counters> -- python -m fine_grained_fp8_quant_amd.profile_workload [--workload prefill]
+
+Quantises the workload's inputs, runs each GEMM mode --reps times, and runs
+one 1 GiB device copy (fgq_debug_copy) whose FETCH_SIZE / WRITE_SIZE
+calibrate the traffic counters (known size: 1 GiB read, 1 GiB written).
+"""
+import argparse
+import os
+import sys
+
+import numpy as np
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "grouped_up", "fused_down"])
+    p.add_argument("--reps", type=int, default=3)
+    p.add_argument("--modes", default="exact,fp8core")
+    args = p.parse_args()
+    import torch
+
+    import fine_grained_fp8_quant_amd as fgq
+    from synth import make_workload
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    d = make_workload(args.workload)
+    if args.workload == "fused_down":
+        fgq.fused_rmsnorm_quant(dev(d["X"]), dev(d["gamma"]), d["eps"])
+    qa, sa = fgq.quant_act_1x128(dev(d["A"]))
+    qw, sw = fgq.quant_w_128x128(dev(d["W"]))
+    off = torch.from_numpy(d["offsets"]).cuda() if "offsets" in d else None
+    for name in args.modes.split(","):
+        mode = fgq.GEMM_EXACT if name == "exact" else fgq.GEMM_FP8_CORE
+        for _ in range(args.reps):
+            if off is None:
+                fgq.gemm_fp8_blockscaled(qa, sa, qw, sw, mode=mode)
+            else:
+                fgq.grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, off, mode=mode)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    fgq.debug_copy(src, dst)
+    torch.cuda.synchronize()
+    print("profile_workload done", args.workload, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -123,6 +123,13 @@ def test_gemm_validation(lib):
     assert gemm(lib, ldc=128) == STRIDE
     assert gemm(lib, sa_skb=-1) == STRIDE
     assert lib.fgq_gemm_workspace_bytes(0, 256, 256) == 0
+    # small M (memory-bound) shapes split K and need an FP32 workspace
+    need = lib.fgq_gemm_workspace_bytes(64, 18432, 7168)
+    assert need > 0 and need % (64 * 18432 * 4) == 0
+    assert lib.fgq_gemm_workspace_bytes(8192, 18432, 7168) == 0
+    assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL     # no workspace
+    assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
+    assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P + 16, ws_bytes=need) == ALIGN
 
 
 def grouped(lib, E=4, R=100, offsets=S, w_es=256 * 256, N=256, K=256, qa=P, ldc=256, mode=0):
