@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quant GB/s (% HBM peak)"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense FP16 MFMA (the exact-product GEMM mode runs on these)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "fine_grained_fp8_quant_amd", "csrc", "gemm.hip")
@@ -200,8 +201,8 @@ def cpu_baseline(args, d):
         blas_threads = 1
     t0 = time.perf_counter()
     if args.workload in ("prefill", "decode"):
-        rows = min(d["M"], 1024)
-        cols = 4096
+        rows = min(d["M"], 4096)
+        cols = 8192 if d["M"] > 64 else d["N"]
         qa, sa = oracle.quant_act_1x128(d["A"][:rows])
         qw, sw = oracle.quant_w_128x128(d["W"][:cols])
         oracle.gemm_ref(qa, sa, qw, sw)
@@ -210,8 +211,8 @@ def cpu_baseline(args, d):
     else:
         e = int(np.argmax(d["counts"]))
         r0 = int(d["offsets"][e])
-        rows = min(int(d["counts"][e]), 1024)
-        cols = min(d["N"], 4096)
+        rows = min(int(d["counts"][e]), 4096)
+        cols = d["N"]
         if args.workload == "fused_down":
             oracle.fused_rmsnorm_quant(d["X"][:rows], d["gamma"], d["eps"])
         qa, sa = oracle.quant_act_1x128(d["A"][r0:r0 + rows])
@@ -228,8 +229,9 @@ def cpu_baseline(args, d):
 
 
 def traffic_for(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    only if the kernel source is unchanged since the counters were taken."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (key "<workload>/<kernel>[<mode>]"), only if the kernel source is
+    unchanged since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -277,6 +279,7 @@ def main():
     gemm_name = [k for k in kern if "gemm" in k][0]
     gemm_ms = kern[gemm_name]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_FP16_TFLOPS if args.mode == "exact" else PEAK_FP8_TFLOPS
     kernels = {}
     for k, ms in kern.items():
         if "gemm" in k:
@@ -286,6 +289,20 @@ def main():
             gbs = quant_bytes[k] / (ms * 1e-3) / 1e9
             kernels[k] = {"ms": ms, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
                           "algorithmic_bytes": quant_bytes[k]}
+    traffic = traffic_for(f"{args.workload}/{gemm_name}[{args.mode}]")
+    if args.workload == "decode":
+        # memory-bound: algorithmic bytes = W codes + weight scales + A codes + act scales + C
+        M, N, K = d["M"], d["N"], d["K"]
+        gbytes = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+        gbs = gbytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": gemm_name, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": gbytes, "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak,
+                    "peak_note": "dense MFMA peak of the contraction's own dtype ("
+                                 + ("fp16" if args.mode == "exact" else "fp8") + ")",
+                    "traffic": traffic}
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
     # the other GEMM accumulation mode, timed alone (not part of the step)
     other = "fp8core" if args.mode == "exact" else "exact"
@@ -312,13 +329,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "e4m3 codes; " + ("products on fp16 matrix cores (exact)" if args.mode == "exact"
+                                   else "fp8 matrix cores") + "; fp32 accumulate",
         "data": "synthetic (seeded, shapes and distributions of the named workload)",
         "config": {"workload": WORKLOAD_TITLES[args.workload], **{k: v for k, v in shape.items() if k != "counts"},
                    "input_sets": len(sets)},
-        "roofline": {"bound": "mfma", "kernel": gemm_name, "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                     "traffic": traffic_for(gemm_name)},
+        "roofline": roofline,
         "kernels": kernels,
         "gemm_mode": args.mode,
         "gemm_other_mode": alt,

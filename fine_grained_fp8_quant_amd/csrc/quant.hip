@@ -133,8 +133,82 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t ldw, int64_t w_bs, 
 // adds the squares of its vectors in turn, value by value, then a butterfly
 // over lane xor 32, 16, ..., 1.  In iteration i the lanes 16g..16g+15 hold
 // exactly tile 4i + g, so the tile max is a 16-lane DPP reduction.
+//
+// Short rows (NI <= 16): the row is widened to binary32 once and normalised
+// in place, and the tile maxima go through a per-wave LDS slot so that lane
+// t does the two correctly rounded divisions of tile t (once per tile rather
+// than once per lane of each 16-lane group).
 template <int NI>
-__global__ __launch_bounds__(256) void k_fused_rmsnorm_quant(
+__global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
+    uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm,
+    int64_t s_skb) {
+  static_assert(NI <= 16, "one tile per lane in the scale pass");
+  __shared__ float tile_slot[4][64];
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  const uint32_t V = K / 8u, ntiles = K / 128u;
+  const uint32_t row = blockIdx.x * 4u + w;
+  if (row >= M) return;  // whole wave leaves together
+  float* slot = tile_slot[w];
+  float y[NI][8];
+  {
+    uint4 v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t vi = lane + 64u * i;
+      v[i] = vi < V ? load_nt16(x + (int64_t)row * ldx + vi * 8u) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) unpack8(v[i], y[i]);
+  }
+  {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (lane + 64u * i < V) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = acc + y[i][j] * y[i][j];  // contraction is off in this file
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d);
+    const float mean = acc / (float)K;
+    const float var = mean + eps;
+    const float rstd = 1.0f / sqrtf(var);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t vi = lane + 64u * i;
+      if (vi < V) {  // V is a multiple of 16: whole 16-lane rows
+        const uint4 gv = *reinterpret_cast<const uint4*>(gamma + vi * 8u);
+        float g[8];
+        unpack8(gv, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[i][j] = (y[i][j] * rstd) * g[j];
+        const float a = max16(absmax8(y[i]));
+        if ((lane & 15u) == 0) slot[vi >> 4] = a;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (lane < ntiles) {
+      float sc, r;
+      group_scales(slot[lane], sc, r);
+      s[(int64_t)row * s_sm + (int64_t)lane * s_skb] = sc;
+      slot[lane] = r;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint8_t* qr = q + (int64_t)row * ldq;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t vi = lane + 64u * i;
+      if (vi < V) store_nt8(qr + vi * 8u, cast8(y[i], slot[vi >> 4]));
+    }
+  }
+}
+
+// Long rows (K up to 16384): the row stays packed BF16 in registers and is
+// widened again for each pass; scales are computed per 16-lane group.
+template <int NI>
+__global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_long(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
     uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm,
     int64_t s_skb) {
@@ -179,29 +253,33 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant(
       const float a = max16(absmax8(y));
       float sc, r;
       group_scales(a, sc, r);
-      *reinterpret_cast<uint2*>(qr + vi * 8u) = cast8(y, r);
+      store_nt8(qr + vi * 8u, cast8(y, r));
       if ((lane & 15u) == 0) s[(int64_t)row * s_sm + (int64_t)(vi >> 4) * s_skb] = sc;
     }
   }
 }
 
+template <int NI>
+static void launch_fused_regs(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t M,
+                              int64_t K, uint8_t* q, int64_t ldq, float* s, int64_t s_sm, int64_t s_skb,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_fused_rmsnorm_quant_regs<NI>, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, st, x, ldx,
+                     gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+}
+
 hipError_t launch_fused_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
                                       int64_t M, int64_t K, uint8_t* q, int64_t ldq, float* s,
                                       int64_t s_sm, int64_t s_skb, hipStream_t st) {
-  const uint32_t grid = (uint32_t)((M + 3) / 4);
   const int64_t ni = (K / 8 + 63) / 64;
-  if (ni <= 4)
-    hipLaunchKernelGGL(k_fused_rmsnorm_quant<4>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
-                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
-  else if (ni <= 8)
-    hipLaunchKernelGGL(k_fused_rmsnorm_quant<8>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
-                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
-  else if (ni <= 16)
-    hipLaunchKernelGGL(k_fused_rmsnorm_quant<16>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
-                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  if (ni <= 2) launch_fused_regs<2>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 4) launch_fused_regs<4>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 8) launch_fused_regs<8>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 12) launch_fused_regs<12>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 14) launch_fused_regs<14>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 16) launch_fused_regs<16>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
   else
-    hipLaunchKernelGGL(k_fused_rmsnorm_quant<32>, dim3(grid), dim3(256), 0, st, x, ldx, gamma, eps,
-                       (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+    hipLaunchKernelGGL(k_fused_rmsnorm_quant_long<32>, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, st, x, ldx,
+                       gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
   return hipGetLastError();
 }
 
