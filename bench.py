@@ -156,7 +156,7 @@ def make_step(args, fgq, d, n_sets, mode):
         if args.workload in ("prefill", "decode"):
             M, K, N = d["M"], d["K"], d["N"]
             o["qa"] = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-            o["sa"] = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+            o["sa"] = fgq.act_scales(M, K, "cuda")
             o["qw"] = torch.empty((N, K), dtype=torch.uint8, device="cuda")
             o["sw"] = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
             o["c"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -166,9 +166,9 @@ def make_step(args, fgq, d, n_sets, mode):
             R, K, N, E = d["R"], d["K"], d["N"], d["E"]
             if args.workload == "fused_down":
                 o["qx"] = torch.empty((d["Mx"], d["Kx"]), dtype=torch.uint8, device="cuda")
-                o["sx"] = torch.empty((d["Mx"], d["Kx"] // 128), dtype=torch.float32, device="cuda")
+                o["sx"] = fgq.act_scales(d["Mx"], d["Kx"], "cuda")
             o["qa"] = torch.empty((R, K), dtype=torch.uint8, device="cuda")
-            o["sa"] = torch.empty((R, K // 128), dtype=torch.float32, device="cuda")
+            o["sa"] = fgq.act_scales(R, K, "cuda")
             o["qw"] = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
             o["sw"] = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda")
             o["c"] = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")

@@ -15,7 +15,10 @@ Functions (same names as the C ABI in include/fgq.h, without the prefix):
 
 Codes are returned as ``torch.uint8`` (``.view(torch.float8_e4m3fn)`` gives
 the FP8 dtype).  Scales may be any strided float32 view; the strides are
-passed to the kernels as they are.
+passed to the kernels as they are.  Activation scales are allocated
+K-block-major by default (storage [K/128, M], returned as the [M, K/128]
+view): a GEMM tile then loads the scales of one K chunk from consecutive
+addresses.
 """
 from __future__ import annotations
 
@@ -24,7 +27,7 @@ import os
 
 __all__ = [
     "FgqError", "load_library", "library_path", "lib",
-    "quant_act_1x128", "quant_w_128x128", "fused_rmsnorm_quant",
+    "quant_act_1x128", "quant_w_128x128", "fused_rmsnorm_quant", "act_scales",
     "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled", "gemm_workspace_bytes",
     "debug_encode_e4m3", "debug_copy", "debug_mfma_16x16x128", "STATUS", "GEMM_EXACT", "GEMM_FP8_CORE",
 ]
@@ -150,6 +153,13 @@ def _codes(t):
     return t
 
 
+def act_scales(M: int, K: int, device):
+    """Uninitialised activation-scale buffer for an [M, K] operand: a float32
+    [M, K/128] view of K-block-major storage (strides (1, M))."""
+    torch = _torch()
+    return torch.empty((K // 128, M), dtype=torch.float32, device=device).t()
+
+
 def quant_act_1x128(x, q=None, s=None, stream=None):
     """1x128 tile quantisation of BF16 ``x [M, K]``.  Optional preallocated
     outputs ``q`` (uint8 [M, K]) and ``s`` (float32 view of shape [M, K/128],
@@ -161,7 +171,7 @@ def quant_act_1x128(x, q=None, s=None, stream=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if s is None:
-        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+        s = act_scales(M, K, x.device)
     _check(lib.fgq_quant_act_1x128(_ptr(x), x.stride(0), M, K, _ptr(q), q.stride(0), _ptr(s),
                                    s.stride(0), s.stride(1), _stream(stream)))
     return q, s
@@ -201,7 +211,7 @@ def fused_rmsnorm_quant(x, gamma, eps: float, q=None, s=None, stream=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if s is None:
-        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+        s = act_scales(M, K, x.device)
     _check(lib.fgq_fused_rmsnorm_quant(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(q),
                                        q.stride(0), _ptr(s), s.stride(0), s.stride(1), _stream(stream)))
     return q, s

@@ -13,23 +13,30 @@
 //      (youlimart.com), paragraph 4: FP8 forward GEMMs of the MoE experts.
 //
 // CDNA4 design (not the pages' Hopper design):
-//   * One 128-wide K chunk is exactly one v_mfma_f32_16x16x128_f8f6f4 per
-//     16x16 output sub-tile, so the chunk's FP8 sum lands in a fresh FP32
-//     temporary (C operand = inline 0) and is promoted at once:
-//     acc = fma(t, sa * sw, acc) on the vector ALU.  The promotion interval
-//     is the scale group, 128, since the scales change every 128 along K.
-//     The vector FMAs of one sub-tile overlap the matrix core's work on the
-//     next (they are independent instructions of the same wave), the
-//     register-level counterpart of the pages' two-warpgroup overlap.
+//   * FP8 matrix-core mode: one 128-wide K chunk is exactly one
+//     v_mfma_f32_16x16x128_f8f6f4 per 16x16 output sub-tile, so the chunk's
+//     FP8 sum lands in a fresh FP32 temporary (C operand = inline 0) and is
+//     promoted at once: acc = fma(t, sa * sw, acc) on the vector ALU.  The
+//     promotion interval is the scale group, 128, since the scales change
+//     every 128 along K.  The vector FMAs of one sub-tile overlap the matrix
+//     core's work on the next (independent instructions of the same wave),
+//     the register-level counterpart of the pages' two-warpgroup overlap.
+//   * Exact mode (default): the same chunk as four K = 32 steps on the FP16
+//     matrix core after an exact E4M3 -> FP16 conversion in registers, then
+//     the same FP32 promotion.  gfx950's FP8 unit truncates inside groups of
+//     eight products; its FP16 unit does not.
 //   * Operands are K-contiguous in HBM and in LDS.  Each lane feeds 32
 //     contiguous K bytes of one row to the MFMA; A and B use the same lane
 //     layout, so whatever order the unit pairs the 128 K positions in, the
 //     sum is the full chunk dot product.
 //   * LDS rows are 128 bytes (one chunk); the 16-byte column c of row r is
-//     stored at column c ^ ((r / 2) mod 8) so that 16 lanes reading 16
-//     consecutive rows at one logical column hit all 64 banks once.
-//   * Global -> register -> LDS double buffering: chunk kb+1 is in flight
-//     while chunk kb is multiplied.
+//     stored at column c ^ ((r / 2) mod 8), which keeps the fragment reads
+//     (16 consecutive rows at one logical column) free of bank conflicts.
+//   * Staging is LDS DMA (global_load_lds, no registers) into NSTAGE stages:
+//     chunk kb + NSTAGE - 1 is in flight while chunk kb is multiplied.  The
+//     per-chunk activation scales are one 4-byte load per row; stored
+//     K-block-major ([K/128][M]) they are contiguous, which is the layout the
+//     quantisers' callers should prefer.
 #include "fgq_device.h"
 #include "fgq_launch.h"
 
@@ -119,106 +126,42 @@ struct TileCfg {
 // over all 64 banks.
 __device__ __forceinline__ int lds_col(int c, int r) { return c ^ ((r >> 1) & 7); }
 
-// One output tile [row_begin, row_begin + BM) x [n0, n0 + BN) over the K
-// chunks [kb_begin, kb_end); rows >= row_end are neither read (their loads
-// repeat row row_end - 1) nor written.  Writes BF16 C, or with PARTIAL the
-// binary32 sums of its chunks to part[m * ldc + n] (split-K workspace).
-template <class C, int MODE, bool PARTIAL = false>
-__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_t lda,
-                                          const float* __restrict__ sa, int64_t sa_sm, int64_t sa_skb,
-                                          int64_t row_begin, int64_t row_end,
-                                          const uint8_t* __restrict__ qw, int64_t ldw,
-                                          const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
-                                          int64_t n0, uint16_t* __restrict__ c, float* __restrict__ part,
-                                          int64_t ldc, int kb_begin, int kb_end, uint8_t* lds) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int l16 = lane & 15, lgrp = lane >> 4;
+// ---- per-chunk arithmetic of one wave.  An engine holds the wave's
+// accumulators; chunk() multiplies the K chunk staged at `base` (layout of
+// TileCfg) into them and store() writes the wave's part of the tile.
 
-  // ---- this lane's DMA sources: slot s = ins * 64 + lane holds row s / 8 at
-  // physical column s % 8, i.e. the logical column whose lds_col is s % 8
-  // (the XOR is its own inverse).  Row = 8 * ins + lane / 8 with ins = wave +
-  // j * NW (NW even), so row & 15 = 8 * (wave & 1) + lane / 8 for every j and
-  // one column offset serves all of them; sources are the tile base plus
-  // 32-bit offsets.
-  static_assert(C::NW % 2 == 0, "instruction parity follows the wave's");
-  const int dcol = lds_col(lane & 7, ((wave & 1) << 3) | (lane >> 3)) * 16;
-  const uint8_t* a_tile = qa + row_begin * lda;
-  const int64_t a_last = row_end - 1 - row_begin;
-  uint32_t a_src[C::A_PER_W];
-#pragma unroll
-  for (int j = 0; j < C::A_PER_W; ++j) {
-    const int r = (wave + j * C::NW) * 8 + (lane >> 3);
-    a_src[j] = (uint32_t)((r < a_last ? r : a_last) * lda) + dcol;
-  }
-  const uint8_t* b_tile = qw + n0 * ldw;
-  uint32_t b_src[C::B_PER_W];
-#pragma unroll
-  for (int j = 0; j < C::B_PER_W; ++j) {
-    const int r = (wave + j * C::NW) * 8 + (lane >> 3);
-    b_src[j] = (uint32_t)((r < C::BN ? r : 0) * ldw) + dcol;
-  }
-  const float* s_src = nullptr;  // activation scales (waves < SA_INS) or weight scales (wave SA_INS)
-  if (wave < C::SA_INS) {
-    int64_t gr = row_begin + wave * 64 + lane;
-    gr = gr < row_end ? gr : row_end - 1;
-    s_src = sa + gr * sa_sm;
-  } else if (wave == C::SA_INS) {
-    s_src = sw + ((n0 >> 7) + (lane < C::NBW ? lane : 0)) * sw_snb;
-  }
-
-  auto issue = [&](int kb, int stage) {
-    uint8_t* base = lds + stage * C::STAGE;
-    const uint8_t* at = a_tile + (int64_t)kb * 128;
-    const uint8_t* bt = b_tile + (int64_t)kb * 128;
-#pragma unroll
-    for (int j = 0; j < C::A_PER_W; ++j) dma16(at + a_src[j], base + (wave + j * C::NW) * 1024);
-#pragma unroll
-    for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
-    if (wave < C::SA_INS) {
-      dma4(s_src + (int64_t)kb * sa_skb, base + C::SA_OFF + wave * 256);
-    } else if (wave == C::SA_INS) {
-      if (lane < C::NBW) dma4(s_src + (int64_t)kb * sw_skb, base + C::SW_OFF);
-    } else if (lane == 0) {
-      dma4(sw, base + C::SW_OFF + 128);  // dummy: keeps the per-wave DMA count uniform
-    }
-  };
-
+// 16x16 sub-tiles: FP8 matrix core (MODE 1), or exact products as four
+// K = 32 steps on the FP16 matrix core (MODE 0).  Lane (l16, lgrp) feeds row
+// l16 of a sub-tile with code bytes 32 lgrp ... 32 lgrp + 31 of the chunk.
+template <class C, int MODE>
+struct Engine16 {
   v4f acc[C::TM][C::TN];
-#pragma unroll
-  for (int mi = 0; mi < C::TM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < C::TN; ++ni) acc[mi][ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  int wm, wn, l16, lgrp;
+  int a_off0, a_off1, b_off0, b_off1, sa_off, sw_idx;
 
-  // LDS byte offsets of this lane's fragment rows: 32 contiguous code bytes
-  // (logical columns 2*lgrp, 2*lgrp + 1 of the 128-byte chunk row).  Sub-tile
-  // rows step by 16, which keeps row & 15, so sub-tiles are base + 2048 * i.
-  // Wave tile origins are multiples of 16 rows as well.
-  const int c0 = lgrp * 2;
-  const int a_off0 = (wm * C::WM + l16) * 128 + (lds_col(c0, l16) << 4);
-  const int a_off1 = (wm * C::WM + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
-  const int b_off0 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0, l16) << 4);
-  const int b_off1 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
-  const int sa_off = C::SA_OFF + (wm * C::WM + lgrp * 4) * 4;
-  const int sw_idx = (wn * C::WN) / 128;
-
-  // NSTAGE-deep pipeline: chunk kb + NSTAGE - 1 is requested while chunk kb
-  // is multiplied.  At the top of iteration kb, the wait leaves the chunks
-  // issued after kb in flight; the barrier then publishes chunk kb to every
-  // wave and frees the stage of chunk kb - 1, which the next request reuses.
+  __device__ __forceinline__ Engine16(int wave, int lane) {
+    wm = wave / C::WAVES_N;
+    wn = wave % C::WAVES_N;
+    l16 = lane & 15;
+    lgrp = lane >> 4;
 #pragma unroll
-  for (int p = 0; p < C::NSTAGE - 1; ++p)
-    if (kb_begin + p < kb_end) issue(kb_begin + p, p);
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const int it = kb - kb_begin;
-    const int stage = it % C::NSTAGE;
-    if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
-    barrier_no_drain();
-    if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-    const uint8_t* base = lds + stage * C::STAGE;
+    for (int mi = 0; mi < C::TM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) acc[mi][ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    // LDS byte offsets of this lane's fragment rows: logical columns 2 lgrp
+    // and 2 lgrp + 1 of the 128-byte chunk row.  Sub-tile rows step by 16,
+    // which keeps row & 15, so sub-tiles are base + 2048 * i; wave tile
+    // origins are multiples of 16 rows as well.
+    const int c0 = lgrp * 2;
+    a_off0 = (wm * C::WM + l16) * 128 + (lds_col(c0, l16) << 4);
+    a_off1 = (wm * C::WM + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
+    b_off0 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0, l16) << 4);
+    b_off1 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
+    sa_off = C::SA_OFF + (wm * C::WM + lgrp * 4) * 4;
+    sw_idx = (wn * C::WN) / 128;
+  }
+
+  __device__ __forceinline__ void chunk(const uint8_t* base) {
     const float swv = reinterpret_cast<const float*>(base + C::SW_OFF)[sw_idx];
     if constexpr (MODE == 1) {
       // FP8 matrix core: one instruction per 16x16 sub-tile and chunk
@@ -306,25 +249,115 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
     }
   }
 
-  // epilogue: lane holds rows lgrp*4 + i, column l16 of each 16x16 sub-tile
+  // lane holds rows lgrp*4 + i, column l16 of each 16x16 sub-tile
+  template <bool PARTIAL>
+  __device__ __forceinline__ void store(int64_t row_begin, int64_t row_end, int64_t n0, uint16_t* __restrict__ c,
+                                        float* __restrict__ part, int64_t ldc) {
 #pragma unroll
-  for (int mi = 0; mi < C::TM; ++mi) {
+    for (int mi = 0; mi < C::TM; ++mi) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t gr = row_begin + wm * C::WM + mi * 16 + lgrp * 4 + i;
-      if (gr < row_end) {
-        if constexpr (PARTIAL) {
-          float* prow = part + gr * ldc + n0 + wn * C::WN + l16;
+      for (int i = 0; i < 4; ++i) {
+        const int64_t gr = row_begin + wm * C::WM + mi * 16 + lgrp * 4 + i;
+        if (gr < row_end) {
+          if constexpr (PARTIAL) {
+            float* prow = part + gr * ldc + n0 + wn * C::WN + l16;
 #pragma unroll
-          for (int ni = 0; ni < C::TN; ++ni) prow[ni * 16] = acc[mi][ni][i];
-        } else {
-          uint16_t* crow = c + gr * ldc + n0 + wn * C::WN + l16;
+            for (int ni = 0; ni < C::TN; ++ni) prow[ni * 16] = acc[mi][ni][i];
+          } else {
+            uint16_t* crow = c + gr * ldc + n0 + wn * C::WN + l16;
 #pragma unroll
-          for (int ni = 0; ni < C::TN; ++ni) crow[ni * 16] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+            for (int ni = 0; ni < C::TN; ++ni) crow[ni * 16] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+          }
         }
       }
     }
   }
+};
+
+// One output tile [row_begin, row_begin + BM) x [n0, n0 + BN) over the K
+// chunks [kb_begin, kb_end); rows >= row_end are neither read (their loads
+// repeat row row_end - 1) nor written.  Writes BF16 C, or with PARTIAL the
+// binary32 sums of its chunks to part[m * ldc + n] (split-K workspace).
+template <class C, int MODE, bool PARTIAL = false>
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_t lda,
+                                          const float* __restrict__ sa, int64_t sa_sm, int64_t sa_skb,
+                                          int64_t row_begin, int64_t row_end,
+                                          const uint8_t* __restrict__ qw, int64_t ldw,
+                                          const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
+                                          int64_t n0, uint16_t* __restrict__ c, float* __restrict__ part,
+                                          int64_t ldc, int kb_begin, int kb_end, uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- this lane's DMA sources: slot s = ins * 64 + lane holds row s / 8 at
+  // physical column s % 8, i.e. the logical column whose lds_col is s % 8
+  // (the XOR is its own inverse).  Row = 8 * ins + lane / 8 with ins = wave +
+  // j * NW (NW even), so row & 15 = 8 * (wave & 1) + lane / 8 for every j and
+  // one column offset serves all of them; sources are the tile base plus
+  // 32-bit offsets.
+  static_assert(C::NW % 2 == 0, "instruction parity follows the wave's");
+  const int dcol = lds_col(lane & 7, ((wave & 1) << 3) | (lane >> 3)) * 16;
+  const uint8_t* a_tile = qa + row_begin * lda;
+  const int64_t a_last = row_end - 1 - row_begin;
+  uint32_t a_src[C::A_PER_W];
+#pragma unroll
+  for (int j = 0; j < C::A_PER_W; ++j) {
+    const int r = (wave + j * C::NW) * 8 + (lane >> 3);
+    a_src[j] = (uint32_t)((r < a_last ? r : a_last) * lda) + dcol;
+  }
+  const uint8_t* b_tile = qw + n0 * ldw;
+  uint32_t b_src[C::B_PER_W];
+#pragma unroll
+  for (int j = 0; j < C::B_PER_W; ++j) {
+    const int r = (wave + j * C::NW) * 8 + (lane >> 3);
+    b_src[j] = (uint32_t)((r < C::BN ? r : 0) * ldw) + dcol;
+  }
+  const float* s_src = nullptr;  // activation scales (waves < SA_INS) or weight scales (wave SA_INS)
+  if (wave < C::SA_INS) {
+    int64_t gr = row_begin + wave * 64 + lane;
+    gr = gr < row_end ? gr : row_end - 1;
+    s_src = sa + gr * sa_sm;
+  } else if (wave == C::SA_INS) {
+    s_src = sw + ((n0 >> 7) + (lane < C::NBW ? lane : 0)) * sw_snb;
+  }
+
+  auto issue = [&](int kb, int stage) {
+    uint8_t* base = lds + stage * C::STAGE;
+    const uint8_t* at = a_tile + (int64_t)kb * 128;
+    const uint8_t* bt = b_tile + (int64_t)kb * 128;
+#pragma unroll
+    for (int j = 0; j < C::A_PER_W; ++j) dma16(at + a_src[j], base + (wave + j * C::NW) * 1024);
+#pragma unroll
+    for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
+    if (wave < C::SA_INS) {
+      dma4(s_src + (int64_t)kb * sa_skb, base + C::SA_OFF + wave * 256);
+    } else if (wave == C::SA_INS) {
+      if (lane < C::NBW) dma4(s_src + (int64_t)kb * sw_skb, base + C::SW_OFF);
+    } else if (lane == 0) {
+      dma4(sw, base + C::SW_OFF + 128);  // dummy: keeps the per-wave DMA count uniform
+    }
+  };
+
+  Engine16<C, MODE> eng(wave, lane);
+
+  // NSTAGE-deep pipeline: chunk kb + NSTAGE - 1 is requested while chunk kb
+  // is multiplied.  At the top of iteration kb, the wait leaves the chunks
+  // issued after kb in flight; the barrier then publishes chunk kb to every
+  // wave and frees the stage of chunk kb - 1, which the next request reuses.
+#pragma unroll
+  for (int p = 0; p < C::NSTAGE - 1; ++p)
+    if (kb_begin + p < kb_end) issue(kb_begin + p, p);
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const int it = kb - kb_begin;
+    const int stage = it % C::NSTAGE;
+    if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
+    barrier_no_drain();
+    if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
+    eng.chunk(lds + stage * C::STAGE);
+  }
+  eng.template store<PARTIAL>(row_begin, row_end, n0, c, part, ldc);
 }
 
 // Linear workgroup id -> (m-tile, n-tile).  Workgroups are dealt to the 8

@@ -75,7 +75,7 @@ def _check(c, ref, what, mode, qa=None, sa=None, qw=None, sw=None, rows=None):
     return g
 
 
-def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None, mode=0):
+def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None, mode=0, sa_kmajor=False):
     import torch
     M, K = qa.shape
     N = qw.shape[0]
@@ -86,7 +86,8 @@ def _gemm(fgq, qa, sa, qw, sw, ldc=None, lda=None, mode=0):
     else:
         qa_d = dev_u8(qa)
     cg = Guarded(M, N, torch.bfloat16, ld=ldc)
-    fgq.gemm_fp8_blockscaled(qa_d, dev_f32(sa), dev_u8(qw), dev_f32(sw), out=cg.view, mode=mode)
+    sa_d = dev_f32(np.ascontiguousarray(sa.T)).t() if sa_kmajor else dev_f32(sa)
+    fgq.gemm_fp8_blockscaled(qa_d, sa_d, dev_u8(qw), dev_f32(sw), out=cg.view, mode=mode)
     torch.cuda.synchronize()
     cg.check_canaries()
     return host_bf16_f64(cg.view)
@@ -152,6 +153,21 @@ def test_gemm_shapes_oracle_operands(fgq_gpu, M, N, K, lda, ldc, mode):
     ref = oracle.gemm_ref(qa, sa, qw, sw)
     c = _gemm(fgq_gpu, qa, sa, qw, sw, ldc=ldc, lda=lda, mode=mode)
     _check(c, ref, f"gemm {M}x{N}x{K}", mode, qa, sa, qw, sw)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K", [(129, 256, 384), (300, 512, 1024), (64, 128, 7168)])
+def test_gemm_scale_layouts_agree(fgq_gpu, M, N, K, mode):
+    """Activation scales stored K-block-major (strides (1, M)) give the same
+    bits as row-major storage, and pass the gate."""
+    a = normal_bf16((M, K), 1.0, rng_for(8, M))
+    w = normal_bf16((N, K), 0.02, rng_for(8, N + 1))
+    qa, sa = oracle.quant_act_1x128(a)
+    qw, sw = oracle.quant_w_128x128(w)
+    c_row = _gemm(fgq_gpu, qa, sa, qw, sw, mode=mode)
+    c_kmaj = _gemm(fgq_gpu, qa, sa, qw, sw, mode=mode, sa_kmajor=True)
+    assert np.array_equal(c_row, c_kmaj)
+    _check(c_kmaj, oracle.gemm_ref(qa, sa, qw, sw), f"gemm {M}x{N}x{K} K-major scales", mode, qa, sa, qw, sw)
 
 
 @pytest.mark.parametrize("mode", MODES)
