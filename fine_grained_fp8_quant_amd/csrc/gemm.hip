@@ -381,7 +381,7 @@ __device__ __forceinline__ void tile_of(int bid, int G, int tiles_m, int& tm, in
 using BigCfg = TileCfg<256, 256, 2, 4>;      // FP8 matrix core, large M
 using BigExactCfg = TileCfg<192, 256, 2, 4>; // exact products, large M (FP16 operands need more registers)
 using SmallCfg = TileCfg<64, 128, 1, 4>;
-using SplitCfg = TileCfg<64, 64, 1, 4, 4>;   // split-K, memory-bound small M: 4-deep prefetch, 2 per CU
+using SplitCfg = TileCfg<64, 128, 1, 4, 3>;  // split-K, memory-bound small M: 3 stages, 2 per CU
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict__ qa, int64_t lda,
@@ -456,7 +456,9 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   p.tiles_n = (int)(N / SplitCfg::BN);
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   const int KB = (int)(K / 128);
-  int S = (int)((1024 + tiles - 1) / tiles);  // aim at >= 1024 workgroups (two per CU at a time)
+  // one round of workgroups at two per CU (512): a second, partly filled
+  // round and short splits both cost more than the deeper reduction saves
+  int S = (int)(512 / tiles);
   if (S > KB / 4) S = KB / 4;                 // at least 4 chunks per split
   if (S > 16) S = 16;
   p.S = S < 2 ? 1 : S;
