@@ -137,16 +137,29 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t ldw, int64_t w_bs, 
 // Short rows (NI <= 16): the row is widened to binary32 once and normalised
 // in place, and the tile maxima go through a per-wave LDS slot so that lane
 // t does the two correctly rounded divisions of tile t (once per tile rather
-// than once per lane of each 16-lane group).
-template <int NI>
+// than once per lane of each 16-lane group).  gamma is widened into LDS once
+// per workgroup; FULL drops the bounds guards when K = 512 NI.
+template <int NI, bool FULL>
 __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
     uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm,
     int64_t s_skb) {
   static_assert(NI <= 16, "one tile per lane in the scale pass");
   __shared__ float tile_slot[4][64];
+  // gamma widened once per workgroup (not once per row): plane 0 holds
+  // values 0..3 of each 8-value vector, plane 1 values 4..7, so a lane's
+  // 16-byte reads sit at a 16-byte stride (no bank conflicts)
+  __shared__ __attribute__((aligned(16))) float gsh[2][NI * 64 * 4];
   const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-  const uint32_t V = K / 8u, ntiles = K / 128u;
+  // FULL: K == 512 NI, every lane owns all NI of its vectors
+  const uint32_t V = FULL ? NI * 64u : K / 8u, ntiles = K / 128u;
+  for (uint32_t vi = threadIdx.x; vi < V; vi += 256u) {
+    float g[8];
+    unpack8(*reinterpret_cast<const uint4*>(gamma + vi * 8u), g);
+    *reinterpret_cast<float4*>(&gsh[0][vi * 4u]) = make_float4(g[0], g[1], g[2], g[3]);
+    *reinterpret_cast<float4*>(&gsh[1][vi * 4u]) = make_float4(g[4], g[5], g[6], g[7]);
+  }
+  __syncthreads();  // before any wave of the workgroup may leave
   const uint32_t row = blockIdx.x * 4u + w;
   if (row >= M) return;  // whole wave leaves together
   float* slot = tile_slot[w];
@@ -156,7 +169,7 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t vi = lane + 64u * i;
-      v[i] = vi < V ? load_nt16(x + (int64_t)row * ldx + vi * 8u) : make_uint4(0, 0, 0, 0);
+      v[i] = (FULL || vi < V) ? load_nt16(x + (int64_t)row * ldx + vi * 8u) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) unpack8(v[i], y[i]);
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if (lane + 64u * i < V) {
+      if (FULL || lane + 64u * i < V) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc = acc + y[i][j] * y[i][j];  // contraction is off in this file
       }
@@ -178,10 +191,10 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t vi = lane + 64u * i;
-      if (vi < V) {  // V is a multiple of 16: whole 16-lane rows
-        const uint4 gv = *reinterpret_cast<const uint4*>(gamma + vi * 8u);
-        float g[8];
-        unpack8(gv, g);
+      if (FULL || vi < V) {  // V is a multiple of 16: whole 16-lane rows
+        const float4 g0 = *reinterpret_cast<const float4*>(&gsh[0][vi * 4u]);
+        const float4 g1 = *reinterpret_cast<const float4*>(&gsh[1][vi * 4u]);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) y[i][j] = (y[i][j] * rstd) * g[j];
         const float a = max16(absmax8(y[i]));
@@ -200,7 +213,7 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t vi = lane + 64u * i;
-      if (vi < V) store_nt8(qr + vi * 8u, cast8(y[i], slot[vi >> 4]));
+      if (FULL || vi < V) store_nt8(qr + vi * 8u, cast8(y[i], slot[vi >> 4]));
     }
   }
 }
@@ -263,8 +276,13 @@ template <int NI>
 static void launch_fused_regs(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t M,
                               int64_t K, uint8_t* q, int64_t ldq, float* s, int64_t s_sm, int64_t s_skb,
                               hipStream_t st) {
-  hipLaunchKernelGGL(k_fused_rmsnorm_quant_regs<NI>, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, st, x, ldx,
-                     gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  const dim3 grid((uint32_t)((M + 3) / 4));
+  if (K == 512 * NI)  // rows that fill the registers exactly: no per-vector guards
+    hipLaunchKernelGGL((k_fused_rmsnorm_quant_regs<NI, true>), grid, dim3(256), 0, st, x, ldx,
+                       gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  else
+    hipLaunchKernelGGL((k_fused_rmsnorm_quant_regs<NI, false>), grid, dim3(256), 0, st, x, ldx,
+                       gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
 }
 
 hipError_t launch_fused_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
