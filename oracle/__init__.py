@@ -22,6 +22,8 @@ numbers, so a passage is located by page and paragraph):
     accumulation: P2 paragraph 3, P4 paragraph 4, P1 paragraph 4.
   * normalisation fused with the FP8 cast, norm kept in higher precision:
     P3 paragraph 3, P2 paragraph 1.
+  * activations quantised to FP8 before they are dispatched to the MoE
+    experts: P2 paragraph 4; 8 routed experts per token: P3 paragraph 4.
 
 The pages fix neither the FP8 format nor the constant; the workload
 definition fixes E4M3 and ``scale = amax / 448``.  Every other open point is
@@ -59,4 +61,8 @@ from .gemm import (  # noqa: F401
     gemm_gate,
     gemm_ref,
     grouped_gemm_ref,
+)
+from .dispatch import (  # noqa: F401
+    dispatch_ref,
+    quant_dispatch_ref,
 )

@@ -10,5 +10,6 @@ from .workloads import (  # noqa: F401
     make_workload,
     normal_bf16,
     rng_for,
+    route_ids,
     zipf_counts,
 )

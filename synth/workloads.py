@@ -1,4 +1,4 @@
-"""The five MoE-transformer-shaped synthetic workloads, seeded.
+"""The MoE-transformer-shaped synthetic workloads, seeded.
 
 Every tensor is drawn from ``numpy.random.default_rng([seed, key])`` with a
 fixed key per tensor role, so that the decode and prefill workloads share
@@ -21,6 +21,10 @@ Readings of the workload descriptions (the descriptions give no more):
   * Zipf(s=1.1) expert counts: see ``zipf_counts``.
   * The grouped down-projection continues the 16384-row RMSNorm batch: it
     routes 16384 rows, with its own ``N(0, 1)`` activations ``[16384, 2048]``.
+  * The dispatch workload routes 4096 tokens to 8 of 32 experts each (the
+    pages activate 8 routed experts per token), so it produces the 32768
+    routed rows of the grouped up-projection; expert popularity follows the
+    same Zipf(1.1) profile (see ``route_ids``).
 """
 from __future__ import annotations
 
@@ -33,6 +37,7 @@ _KEYS = {
     "A_prefill": 20, "rowscale_prefill": 21,
     "counts_up": 30, "A_up": 31, "W_up": 32,
     "X_norm": 40, "gamma_norm": 41, "counts_down": 42, "A_down": 43, "W_down": 44,
+    "X_dispatch": 50, "ids_dispatch": 51,
 }
 
 
@@ -104,6 +109,31 @@ def zipf_counts(total_rows: int, n_experts: int, s: float, rng: np.random.Genera
     return counts
 
 
+def route_ids(n_tokens: int, topk: int, n_experts: int, s: float, rng: np.random.Generator,
+              drop: float = 0.0) -> np.ndarray:
+    """Routing decisions: ``int32 [n_tokens, topk]`` expert ids.
+
+    Each token picks ``topk`` distinct experts, drawn without replacement
+    with probabilities ``~ rank**-s`` (ranks assigned to expert ids by a
+    random permutation), by the Gumbel-top-k construction: the ``topk``
+    largest of ``log p_e + G_e`` with i.i.d. standard Gumbel ``G_e``.  The
+    slot order within a token is the draw order.  A fraction ``drop`` of the
+    (token, slot) entries is then set to -1 (not routed).
+    """
+    ranks = np.arange(1, n_experts + 1, dtype=np.float64)
+    p = ranks ** (-float(s))
+    p /= p.sum()
+    perm = rng.permutation(n_experts)
+    logp = np.empty(n_experts)
+    logp[perm] = np.log(p)
+    g = rng.gumbel(size=(int(n_tokens), n_experts))
+    keys = logp[None, :] + g
+    ids = np.argsort(-keys, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    if drop > 0.0:
+        ids[rng.random(ids.shape) < drop] = -1
+    return ids
+
+
 def offsets_from_counts(counts: np.ndarray) -> np.ndarray:
     """``[0, cumsum(counts)]`` as int32 (row offsets of each expert)."""
     off = np.zeros(len(counts) + 1, dtype=np.int64)
@@ -119,6 +149,8 @@ WORKLOADS = {
     "grouped_up": "32 experts, 32768 Zipf(1.1) rows; A [32768,7168] N(0,1); W [32,4096,7168] N(0,0.02)",
     "fused_down": "RMSNorm(eps 1e-6, gamma U(0.5,1.5)) + quant of X [16384,7168] N(0,2); "
                   "grouped down: 32 experts, 16384 Zipf(1.1) rows, A [16384,2048] N(0,1), W [32,7168,2048] N(0,0.02)",
+    "dispatch": "quantise-then-dispatch: X [4096,7168] N(0,1) tokens, top-8 of 32 experts per token "
+                "(Zipf(1.1) expert popularity) -> 32768 expert-ordered FP8 rows",
 }
 
 
@@ -194,6 +226,14 @@ def make_workload(name: str, seed: int = 0, rows: int | None = None, parts=None)
             d["A"] = normal_bf16((R, K), 1.0, rng_for(seed, "A_down"))
         if want("W"):
             d["W"] = normal_bf16((E, N, K), 0.02, rng_for(seed, "W_down"))
+    elif name == "dispatch":
+        T, topk, E, K = 4096, 8, 32, 7168
+        T = T if rows is None else rows
+        d.update(T=T, topk=topk, E=E, K=K)
+        if want("ids"):
+            d["ids"] = route_ids(T, topk, E, 1.1, rng_for(seed, "ids_dispatch"))
+        if want("X"):
+            d["X"] = normal_bf16((T, K), 1.0, rng_for(seed, "X_dispatch"))
     else:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
     return d
