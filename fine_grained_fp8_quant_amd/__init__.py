@@ -12,6 +12,7 @@ Functions (same names as the C ABI in include/fgq.h, without the prefix):
     fused_rmsnorm_quant(x, gamma, eps)     -> (q, s) as quant_act_1x128
     gemm_fp8_blockscaled(qa, sa, qw, sw)   -> c bfloat16 [M, N]
     grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets) -> c bfloat16 [R, N]
+    quant_dispatch_1x128(x, ids, E)        -> (q, s, offsets, row_src, dest): FP8 rows grouped by expert
 
 Codes are returned as ``torch.uint8`` (``.view(torch.float8_e4m3fn)`` gives
 the FP8 dtype).  Scales may be any strided float32 view; the strides are
@@ -29,6 +30,7 @@ __all__ = [
     "FgqError", "load_library", "library_path", "lib",
     "quant_act_1x128", "quant_w_128x128", "fused_rmsnorm_quant", "act_scales",
     "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled", "gemm_workspace_bytes",
+    "quant_dispatch_1x128", "quant_dispatch_workspace_bytes",
     "debug_encode_e4m3", "debug_copy", "debug_mfma_16x16x128", "STATUS", "GEMM_EXACT", "GEMM_FP8_CORE",
 ]
 
@@ -69,6 +71,9 @@ _SIGNATURES = {
     "fgq_grouped_gemm_fp8_blockscaled": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                          _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _st, _vp],
     "fgq_gemm_workspace_bytes": [_i64, _i64, _i64],
+    "fgq_quant_dispatch_1x128": [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                                 _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+    "fgq_quant_dispatch_workspace_bytes": [_i64, _i64, _i64],
     "fgq_status_string": [_st],
     "fgq_last_hip_error": [],
     "fgq_abi_version": [],
@@ -78,6 +83,7 @@ _SIGNATURES = {
 }
 _RESTYPES = {
     "fgq_gemm_workspace_bytes": ctypes.c_size_t,
+    "fgq_quant_dispatch_workspace_bytes": ctypes.c_size_t,
     "fgq_status_string": ctypes.c_char_p,
 }
 
@@ -215,6 +221,49 @@ def fused_rmsnorm_quant(x, gamma, eps: float, q=None, s=None, stream=None):
     _check(lib.fgq_fused_rmsnorm_quant(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(q),
                                        q.stride(0), _ptr(s), s.stride(0), s.stride(1), _stream(stream)))
     return q, s
+
+
+def quant_dispatch_workspace_bytes(T: int, topk: int, E: int) -> int:
+    load_library()
+    return int(lib.fgq_quant_dispatch_workspace_bytes(T, topk, E))
+
+
+def quant_dispatch_1x128(x, ids, n_experts: int, q=None, s=None, offsets=None, row_src=None, dest=None,
+                         workspace=None, stream=None):
+    """Quantise-then-dispatch of BF16 tokens ``x [T, K]`` routed by ``ids``
+    (int32 ``[T, topk]``, device) to ``n_experts`` experts.  Returns
+    ``(q, s, offsets, row_src, dest)``: ``q`` uint8 and ``s`` float32 with
+    room for ``T * topk`` rows (rows of expert e are
+    ``offsets[e] .. offsets[e+1] - 1``), ``offsets`` int32 ``[E + 1]``,
+    ``row_src`` and ``dest`` int32 ``[T * topk]`` (see include/fgq.h)."""
+    torch = _torch()
+    load_library()
+    _need(x, torch.bfloat16, "x")
+    _need(ids, torch.int32, "ids")
+    T, K = x.shape
+    if ids.dim() != 2 or ids.shape[0] != T or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 [T, topk] tensor")
+    topk = ids.shape[1]
+    R = T * topk
+    dev = x.device
+    if q is None:
+        q = torch.empty((R, K), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = act_scales(R, K, dev)
+    if offsets is None:
+        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    if row_src is None:
+        row_src = torch.empty(R, dtype=torch.int32, device=dev)
+    if dest is None:
+        dest = torch.empty(R, dtype=torch.int32, device=dev)
+    need = quant_dispatch_workspace_bytes(T, topk, n_experts)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.fgq_quant_dispatch_1x128(_ptr(x), x.stride(0), T, K, _ptr(ids), topk, n_experts, _ptr(q),
+                                        q.stride(0), _ptr(s), s.stride(0), s.stride(1), _ptr(offsets),
+                                        _ptr(row_src), _ptr(dest), _ptr(workspace), ws_bytes, _stream(stream)))
+    return q, s, offsets, row_src, dest
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:

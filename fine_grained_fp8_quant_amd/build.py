@@ -29,6 +29,7 @@ COMMON = [
 ]
 SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
+    "dispatch.hip": ["-ffp-contract=off"],
     # MFMA results straight into VGPRs: the per-chunk promotion FMA reads them
     # on the vector ALU, which cannot read AGPRs without an extra move.
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

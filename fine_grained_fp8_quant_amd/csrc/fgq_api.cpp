@@ -163,6 +163,37 @@ const char* fgq_status_string(fgq_status_t status) {
 
 int32_t fgq_last_hip_error(void) { return g_last_hip_error; }
 
+fgq_status_t fgq_quant_dispatch_1x128(const void* x, int64_t ldx, int64_t T, int64_t K, const int32_t* ids,
+                                      int64_t topk, int64_t E, void* q, int64_t ldq, float* s, int64_t s_sm,
+                                      int64_t s_skb, int32_t* offsets, int32_t* row_src, int32_t* dest,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 0 || topk < 1 || E < 1) return FGQ_ERR_SHAPE;
+  if (K % 128 != 0 || E > 4096) return FGQ_ERR_UNSUPPORTED;
+  if (T >= kMaxTiles || topk >= kMaxTiles || T * topk >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
+  if (!offsets) return FGQ_ERR_NULL;
+  if (!aligned(offsets, 4)) return FGQ_ERR_ALIGN;
+  if (T > 0) {
+    if (!ids || !row_src || !dest) return FGQ_ERR_NULL;
+    if (!aligned(ids, 4) || !aligned(row_src, 4) || !aligned(dest, 4)) return FGQ_ERR_ALIGN;
+    const fgq_status_t st = check_act_io(x, ldx, T, K, q, ldq, s, s_sm, s_skb);
+    if (st != FGQ_OK) return st;
+    const size_t need = fgq::dispatch_workspace_bytes(T, topk, E);
+    if (need > 0) {
+      if (!workspace) return FGQ_ERR_NULL;
+      if (workspace_bytes < need) return FGQ_ERR_SHAPE;
+      if (!aligned(workspace, 256)) return FGQ_ERR_ALIGN;
+    }
+  }
+  return from_hip(fgq::launch_quant_dispatch_1x128(static_cast<const uint16_t*>(x), ldx, T, K, ids, topk, E,
+                                                   static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb, offsets,
+                                                   row_src, dest, workspace, as_stream(stream)));
+}
+
+size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
+  if (T < 0 || topk < 1 || E < 1 || T >= kMaxTiles || topk >= kMaxTiles || T * topk >= kMaxTiles) return 0;
+  return fgq::dispatch_workspace_bytes(T, topk, E);
+}
+
 int32_t fgq_abi_version(void) { return FGQ_ABI_VERSION; }
 
 fgq_status_t fgq_debug_encode_e4m3(uint32_t start, int64_t n, void* out, void* stream) {

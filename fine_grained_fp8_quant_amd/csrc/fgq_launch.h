@@ -35,6 +35,13 @@ hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, c
                                                uint16_t* c, int64_t ldc, int64_t N, int64_t K, int mode,
                                                hipStream_t st);
 
+hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                       const int32_t* ids, int64_t topk, int64_t E, uint8_t* q, int64_t ldq,
+                                       float* s, int64_t s_sm, int64_t s_skb, int32_t* offsets,
+                                       int32_t* row_src, int32_t* dest, void* workspace, hipStream_t st);
+
+size_t dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+
 hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_debug_mfma(const uint8_t* a, const uint8_t* b, const float* cin, float* d, hipStream_t st);

@@ -57,7 +57,7 @@ enum {
   FGQ_ERR_HIP = 6          /* a HIP launch failed; see fgq_last_hip_error() */
 };
 
-#define FGQ_ABI_VERSION 1
+#define FGQ_ABI_VERSION 2
 
 /*
  * fgq_quant_act_1x128 -- online activation quantisation, one scale per
@@ -204,6 +204,50 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
                                               const int32_t* offsets, int64_t E, int64_t total_rows,
                                               void* c, int64_t ldc, int64_t N, int64_t K, int32_t mode,
                                               void* stream);
+
+/*
+ * fgq_quant_dispatch_1x128 -- quantise-then-dispatch: the activations that
+ * enter the MoE up-projection are quantised to FP8 and handed to the experts
+ * in that form [P2 paragraph 4]; each token goes to topk experts
+ * [P3 paragraph 4].
+ *
+ * Pair i = t * topk + j (token t < T, slot j < topk) whose id ids[i] lies in
+ * [0, E) becomes one output row; pairs with other ids are not routed.  Rows
+ * are grouped by expert and, inside an expert, ordered by increasing i, so
+ * the output is unique:
+ *     offsets[e] .. offsets[e+1]-1   rows of expert e; offsets[0] = 0 and
+ *                                    offsets[E] = R, the number of routed pairs
+ *     row_src[r] = i                 for every row r < R
+ *     dest[i] = r, or -1             for every pair i < T * topk
+ *     q[r, :], s[r, :]               the 1x128 quantisation of token row
+ *                                    i / topk: bit-identical to
+ *                                    fgq_quant_act_1x128 of that row.
+ * This is the row layout fgq_grouped_gemm_fp8_blockscaled consumes (pass
+ * offsets, and T * topk as total_rows); row_src and dest are the maps a
+ * combine step needs.
+ *
+ *   x        BF16 [T, K], row stride ldx (>= K, multiple of 8); 16-byte aligned.
+ *   ids      DEVICE int32 [T, topk], row-major (row stride topk); 4-byte aligned.
+ *   q        E4M3 output with room for T * topk rows, row stride ldq (>= K,
+ *            multiple of 16); 16-byte aligned.  Rows >= R are not written.
+ *   s        float output, s[r * s_sm + kb * s_skb], room for T * topk rows.
+ *   offsets  DEVICE int32 [E + 1] output, written also when T = 0.
+ *   row_src  DEVICE int32 [T * topk] output; entries >= R are not written.
+ *   dest     DEVICE int32 [T * topk] output.
+ *   workspace / workspace_bytes: scratch the caller provides; at least
+ *            fgq_quant_dispatch_workspace_bytes(T, topk, E) bytes, 256-byte
+ *            aligned (may be NULL when that is 0).
+ *   K a multiple of 128; T >= 0; topk >= 1; 1 <= E <= 4096;
+ *   T * topk < 2^31.  The inputs are read only by the GPU (no host sync).
+ */
+fgq_status_t fgq_quant_dispatch_1x128(const void* x, int64_t ldx, int64_t T, int64_t K,
+                                      const int32_t* ids, int64_t topk, int64_t E, void* q,
+                                      int64_t ldq, float* s, int64_t s_sm, int64_t s_skb,
+                                      int32_t* offsets, int32_t* row_src, int32_t* dest,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fgq_quant_dispatch_1x128 needs (0 = none). */
+size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E);
 
 /* Text for a status code (static storage; never NULL). */
 const char* fgq_status_string(fgq_status_t status);

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("fgq_quant_act_1x128", "fgq_quant_w_128x128", "fgq_fused_rmsnorm_quant",
-              "fgq_gemm_fp8_blockscaled", "fgq_grouped_gemm_fp8_blockscaled"):
+              "fgq_gemm_fp8_blockscaled", "fgq_grouped_gemm_fp8_blockscaled", "fgq_quant_dispatch_1x128"):
         assert n in names
 
 
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fgq_abi_version() == 1
+    assert lib.fgq_abi_version() == 2
     for code in range(7):
         assert lib.fgq_status_string(code)
     assert lib.fgq_status_string(99) == b"unknown status"
@@ -172,3 +172,35 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     finally:
         fgq.lib = saved
     importlib.invalidate_caches()
+
+
+def dispatch(lib, x=P, ldx=256, T=4, K=256, ids=S, topk=2, E=3, q=Q, ldq=256, s=S + 1024, s_sm=1, s_skb=8,
+             off=S + 2048, src=S + 3072, dest=S + 4096, ws=P + 65536, ws_bytes=1 << 20):
+    return lib.fgq_quant_dispatch_1x128(x, ldx, T, K, ids, topk, E, q, ldq, s, s_sm, s_skb, off, src, dest,
+                                        ws, ws_bytes, None)
+
+
+def test_dispatch_validation(lib):
+    assert dispatch(lib, T=-1) == SHAPE
+    assert dispatch(lib, topk=0) == SHAPE
+    assert dispatch(lib, E=0) == SHAPE
+    assert dispatch(lib, E=4097) == UNSUP
+    assert dispatch(lib, K=200) == UNSUP
+    assert dispatch(lib, T=1 << 20, topk=1 << 12) == UNSUP      # 2^32 pairs
+    assert dispatch(lib, off=0) == NULL
+    assert dispatch(lib, off=S + 2050) == ALIGN
+    assert dispatch(lib, ids=0) == NULL
+    assert dispatch(lib, src=0) == NULL
+    assert dispatch(lib, dest=S + 4098) == ALIGN
+    assert dispatch(lib, x=P + 8) == ALIGN
+    assert dispatch(lib, q=0) == NULL
+    assert dispatch(lib, ldq=128) == STRIDE
+    assert dispatch(lib, s_skb=-1) == STRIDE
+    need = lib.fgq_quant_dispatch_workspace_bytes(4, 2, 3)
+    assert need > 0
+    assert dispatch(lib, ws=0) == NULL
+    assert dispatch(lib, ws_bytes=need - 1) == SHAPE
+    assert dispatch(lib, ws=P + 65536 + 16) == ALIGN
+    assert lib.fgq_quant_dispatch_workspace_bytes(0, 8, 32) == 0
+    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32) == 2 * 32 * 32 * 4
+    assert lib.fgq_quant_dispatch_workspace_bytes(-1, 8, 32) == 0
