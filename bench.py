@@ -9,7 +9,10 @@ the BF16 inputs already resident in HBM:
   * decode: the same three calls at A 64x7168;
   * grouped_up: quant A 32768x7168, quant W 32x4096x7168, grouped GEMM;
   * fused_down: fused_rmsnorm_quant(X 16384x7168) + quant A_down
-    16384x2048 + quant W 32x7168x2048 + grouped down-projection GEMM.
+    16384x2048 + quant W 32x7168x2048 + grouped down-projection GEMM;
+  * dispatch: quant_dispatch_1x128 of 4096 tokens routed to 8 of 32 experts
+    each (32768 expert-ordered FP8 rows) + quant W 32x4096x7168 + grouped
+    up-projection GEMM on the dispatched rows.
 Inputs rotate over several buffer sets so the 256 MB last-level cache
 cannot serve one step from the previous one.  `value` is whole-step GEMM
 throughput: GEMM FLOPs per step / step time.  Per-kernel durations come
@@ -43,6 +46,7 @@ WORKLOAD_TITLES = {
     "decode": "decode GEMM 64x7168x18432 (A 1x128 + W 128x128 E4M3 quant + GEMM)",
     "grouped_up": "grouped MoE up-proj 32 experts, 32768 Zipf rows, K 7168, N 4096",
     "fused_down": "fused RMSNorm+quant 16384x7168, grouped MoE down-proj 32 experts, 16384 rows, K 2048, N 7168",
+    "dispatch": "quantise-then-dispatch 4096 tokens x top-8 of 32 experts (K 7168) + grouped MoE up-proj, N 4096",
 }
 
 
@@ -112,6 +116,16 @@ def build_sets(args):
         quant_bytes = {"quant_act_1x128": 3 * R * K + 4 * R * K // 128,
                        "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
         shape = {"E": E, "rows": R, "N": N, "K": K, "counts": d["counts"].tolist()}
+    elif args.workload == "dispatch":
+        X, W = dev_bf16(d["X"]), dev_bf16(d["W"])
+        T, topk, E, K, N = d["T"], d["topk"], d["E"], d["K"], d["N"]
+        ids = torch.from_numpy(d["ids"]).cuda()
+        R = T * topk
+        per_set = X.numel() * 2 + R * K + W.numel() * 3 + R * N * 2
+        flops = 2.0 * R * N * K
+        quant_bytes = {"quant_dispatch_1x128": 2 * T * K + R * K + 4 * R * K // 128 + 4 * R + 4 * (E + 1) + 8 * R,
+                       "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
+        shape = {"tokens": T, "topk": topk, "E": E, "rows": R, "N": N, "K": K}
     else:
         X, G = dev_bf16(d["X"]), dev_bf16(d["gamma"])
         A, W = dev_bf16(d["A"]), dev_bf16(d["W"])
@@ -130,6 +144,10 @@ def build_sets(args):
         if args.workload in ("prefill", "decode", "grouped_up"):
             s["A"] = A if i == 0 else A.clone()
             s["W"] = W if i == 0 else W.clone()
+        elif args.workload == "dispatch":
+            s["X"] = X if i == 0 else X.clone()
+            s["W"] = W if i == 0 else W.clone()
+            s["ids"] = ids
         else:
             s["X"] = X if i == 0 else X.clone()
             s["G"] = G
@@ -162,6 +180,19 @@ def make_step(args, fgq, d, n_sets, mode):
             o["c"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             ws = fgq.gemm_workspace_bytes(M, N, K)
             o["ws"] = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda") if ws else None
+        elif args.workload == "dispatch":
+            T, topk, K, N, E = d["T"], d["topk"], d["K"], d["N"], d["E"]
+            R = T * topk
+            o["qa"] = torch.empty((R, K), dtype=torch.uint8, device="cuda")
+            o["sa"] = fgq.act_scales(R, K, "cuda")
+            o["off"] = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+            o["src"] = torch.empty(R, dtype=torch.int32, device="cuda")
+            o["dest"] = torch.empty(R, dtype=torch.int32, device="cuda")
+            o["dws"] = torch.empty(max(fgq.quant_dispatch_workspace_bytes(T, topk, E), 1), dtype=torch.uint8,
+                                   device="cuda")
+            o["qw"] = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
+            o["sw"] = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda")
+            o["c"] = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
         else:
             R, K, N, E = d["R"], d["K"], d["N"], d["E"]
             if args.workload == "fused_down":
@@ -176,6 +207,15 @@ def make_step(args, fgq, d, n_sets, mode):
 
     def step(i, s, t):
         o = outs[i]
+        if args.workload == "dispatch":
+            t.run("quant_dispatch_1x128",
+                  lambda: fgq.quant_dispatch_1x128(s["X"], s["ids"], d["E"], q=o["qa"], s=o["sa"], offsets=o["off"],
+                                                   row_src=o["src"], dest=o["dest"], workspace=o["dws"]))
+            t.run("quant_w_128x128", lambda: fgq.quant_w_128x128(s["W"], q=o["qw"], s=o["sw"]))
+            t.run("grouped_gemm_fp8_blockscaled",
+                  lambda: fgq.grouped_gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], o["off"],
+                                                           out=o["c"], mode=mode))
+            return
         if args.workload == "fused_down":
             t.run("fused_rmsnorm_quant", lambda: fgq.fused_rmsnorm_quant(s["X"], s["G"], eps, q=o["qx"], s=o["sx"]))
         t.run("quant_act_1x128", lambda: fgq.quant_act_1x128(s["A"], q=o["qa"], s=o["sa"]))
@@ -208,6 +248,19 @@ def cpu_baseline(args, d):
         oracle.gemm_ref(qa, sa, qw, sw)
         flops = 2.0 * rows * cols * d["K"]
         sample = f"A rows 0..{rows - 1} x W rows 0..{cols - 1}, full K={d['K']}: quant A, quant W, float64 GEMM"
+    elif args.workload == "dispatch":
+        offsets, row_src, _ = oracle.dispatch_ref(d["ids"], d["E"])
+        e = int(np.argmax(np.diff(offsets)))
+        rows = min(int(offsets[e + 1] - offsets[e]), 4096)
+        toks = row_src[offsets[e]:offsets[e] + rows].astype(np.int64) // d["topk"]
+        cols = d["N"]
+        ids_e = np.full((rows, 1), e, np.int32)     # the sampled rows, all routed to expert e
+        qa, sa, _, _, _ = oracle.quant_dispatch_ref(d["X"][toks], ids_e, d["E"])
+        qw, sw = oracle.quant_w_128x128(d["W"][e, :cols])
+        oracle.gemm_ref(qa, sa, qw, sw)
+        flops = 2.0 * rows * cols * d["K"]
+        sample = (f"routing of all {d['T']} tokens, then expert {e}: {rows} dispatched rows x {cols} weight rows, "
+                  f"full K={d['K']}: dispatch quant, quant W, float64 GEMM")
     else:
         e = int(np.argmax(d["counts"]))
         r0 = int(d["offsets"][e])

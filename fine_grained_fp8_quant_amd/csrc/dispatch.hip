@@ -13,14 +13,15 @@
 // expert ordered by i, so the result is unique and deterministic.
 //
 // Four launches on one stream:
-//   1. k_dispatch_count    per block of 1024 pairs, a histogram over experts
+//   1. k_dispatch_count    per block of 256 pairs, a histogram over experts
 //                          (LDS atomics: counts do not depend on order);
 //   2. k_dispatch_scan     one workgroup: expert totals, the exclusive scan
 //                          that gives offsets[], and each block's first row
 //                          per expert;
 //   3. k_dispatch_scatter  one wave per block walks its pairs in index order
-//                          64 at a time; lanes with the same expert are
-//                          ranked by ballot, so positions follow i;
+//                          64 at a time; a lane's rank among the lanes with
+//                          the same expert is counted lane by lane, so
+//                          positions follow i;
 //   4. k_dispatch_quant    1x128 quantisation, each token tile read once and
 //                          its codes and scale stored to every routed row of
 //                          that token (the per-tile arithmetic is the
@@ -31,7 +32,7 @@
 
 namespace fgq {
 
-constexpr int kPairsPerBlock = 1024;
+constexpr int kPairsPerBlock = 256;
 
 // 1. per-block expert histogram: counts[b * E + e]
 __global__ __launch_bounds__(256) void k_dispatch_count(const int32_t* __restrict__ ids, int64_t N, int E,
@@ -70,34 +71,73 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t* sh, int32_t& total) 
   return incl - v;
 }
 
-// 2. offsets[0..E] and base[b * E + e] = first row of expert e in block b.
-// Thread t owns experts t, t + 1024, ... (E <= 4096).
-__global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t* __restrict__ counts, int nb, int E,
-                                                        int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
-  __shared__ int32_t sh[1024];
-  int32_t carry = 0;
-  for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + (int)threadIdx.x;
-    int32_t tot = 0;
-    if (e < E)
-      for (int b = 0; b < nb; ++b) tot += counts[(int64_t)b * E + e];
-    int32_t seg_total;
-    const int32_t excl = block_exclusive_scan(tot, sh, seg_total);
-    const int32_t off = carry + excl;
-    if (e < E) {
-      offsets[e] = off;
-      int32_t run = off;
-      for (int b = 0; b < nb; ++b) {
-        base[(int64_t)b * E + e] = run;
-        run += counts[(int64_t)b * E + e];
-      }
-    }
-    carry += seg_total;
-  }
-  if (threadIdx.x == 0) offsets[E] = carry;
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
 }
 
-// 3. one wave per block: dest[i] (row or -1) and row_src[row] = i
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
+// 2. offsets[0..E] and base[b * E + e] = first row of expert e in block b.
+// 16 waves; wave w handles experts w, w + 16, ...: its lanes sum (then
+// prefix-sum) the expert's block counts 64 blocks at a time.  E <= 4096.
+__global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t* __restrict__ counts, int nb, int E,
+                                                        int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
+  __shared__ int32_t first_row[4096];  // expert totals, then expert offsets
+  __shared__ int32_t sh[1024];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = w; e < E; e += 16) {
+    int32_t t = 0;
+    for (int b = lane; b < nb; b += 64) t += counts[(int64_t)b * E + e];
+    t = wave_sum(t);
+    if (lane == 0) first_row[e] = t;
+  }
+  __syncthreads();
+  // offsets: exclusive scan over experts; thread t owns experts 4t .. 4t + 3
+  int32_t v[4], local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * (int)threadIdx.x + j;
+    v[j] = e < E ? first_row[e] : 0;
+    local += v[j];
+  }
+  int32_t total;
+  int32_t run = block_exclusive_scan(local, sh, total);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * (int)threadIdx.x + j;
+    if (e < E) {
+      offsets[e] = run;
+      first_row[e] = run;
+    }
+    run += v[j];
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  for (int e = w; e < E; e += 16) {
+    int32_t carry = first_row[e];
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int b = b0 + lane;
+      const int32_t c = b < nb ? counts[(int64_t)b * E + e] : 0;
+      const int32_t incl = wave_inclusive_scan(c, lane);
+      if (b < nb) base[(int64_t)b * E + e] = carry + incl - c;
+      carry += __shfl(incl, 63);
+    }
+  }
+}
+
+// 3. one wave per block: dest[i] (row or -1) and row_src[row] = i.  Each
+// lane compares its expert with every lane of the 64-pair round: its rank is
+// the number of lower lanes with the same expert, and the highest such lane
+// moves the expert's LDS counter past the round.
 __global__ __launch_bounds__(64) void k_dispatch_scatter(const int32_t* __restrict__ ids, int64_t N, int E,
                                                          const int32_t* __restrict__ base,
                                                          int32_t* __restrict__ dest, int32_t* __restrict__ row_src) {
@@ -105,25 +145,34 @@ __global__ __launch_bounds__(64) void k_dispatch_scatter(const int32_t* __restri
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
   __syncthreads();
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
   const int64_t i0 = (int64_t)blockIdx.x * kPairsPerBlock;
-  for (int r = 0; r < kPairsPerBlock / 64; ++r) {
+  constexpr int kRounds = kPairsPerBlock / 64;
+  int32_t ev[kRounds];  // all of the block's ids in flight at once
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
     const int64_t i = i0 + r * 64 + lane;
-    const int32_t e = i < N ? ids[i] : -1;
+    ev[r] = i < N ? ids[i] : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t i = i0 + r * 64 + lane;
+    const int32_t e = ev[r];
     const bool valid = i < N && e >= 0 && e < E;
+    const int32_t key = valid ? e : -1 - lane;  // lanes that are not routed match nobody
+    int rank = 0, later = 0;
+#pragma unroll 16
+    for (int l = 0; l < 64; ++l) {
+      const int32_t kl = __builtin_amdgcn_readlane(key, l);
+      rank += (l < lane) & (kl == key);
+      later += (l > lane) & (kl == key);
+    }
     int32_t pos = -1;
-    uint64_t pending = __ballot(valid);
-    while (pending) {  // one pass per distinct expert among the 64 pairs
-      const int leader = __builtin_ctzll(pending);
-      const int32_t el = __builtin_amdgcn_readlane(e, leader);
-      const bool mine = valid && e == el;
-      const uint64_t m = __ballot(mine);
-      const int32_t c0 = cnt[el];
-      if (mine) pos = c0 + __popcll(m & below);
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) cnt[el] = c0 + __popcll(m);
-      __builtin_amdgcn_wave_barrier();
-      pending &= ~m;
+    if (valid) {
+      // one LDS read for all routed lanes, then one write by the last lane
+      // of each expert (the wave executes them in this order)
+      const int32_t c0 = cnt[e];
+      pos = c0 + rank;
+      if (later == 0) cnt[e] = c0 + rank + 1;
     }
     if (i < N) dest[i] = pos;
     if (valid) row_src[pos] = (int32_t)i;
@@ -135,6 +184,9 @@ __global__ __launch_bounds__(64) void k_dispatch_scatter(const int32_t* __restri
 // a 16-lane group holds one tile (16 x 8 BF16 values).
 constexpr int kDispU = 4;
 
+// MAXK > 0: topk <= MAXK, the destination rows of each tile's token are
+// loaded with the tile (no dependent load before each store); MAXK = 0: any topk.
+template <int MAXK>
 __global__ __launch_bounds__(256) void k_dispatch_quant(const uint16_t* __restrict__ x, int64_t ldx, uint32_t KB,
                                                         uint32_t n_tiles, int topk, const int32_t* __restrict__ dest,
                                                         uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
@@ -144,6 +196,7 @@ __global__ __launch_bounds__(256) void k_dispatch_quant(const uint16_t* __restri
   const uint32_t first = blockIdx.x * (16u * kDispU) + grp;
   uint4 v[kDispU];
   uint32_t tt[kDispU], kk[kDispU];
+  int32_t dr[kDispU][MAXK > 0 ? MAXK : 1];
 #pragma unroll
   for (int u = 0; u < kDispU; ++u) {
     uint32_t g = first + 16u * u;
@@ -151,6 +204,10 @@ __global__ __launch_bounds__(256) void k_dispatch_quant(const uint16_t* __restri
     tt[u] = g / KB;
     kk[u] = g - tt[u] * KB;
     v[u] = load_nt16(x + (int64_t)tt[u] * ldx + kk[u] * 128u + lane16 * 8u);
+    if constexpr (MAXK > 0) {
+#pragma unroll
+      for (int j = 0; j < MAXK; ++j) dr[u][j] = j < topk ? dest[(int64_t)tt[u] * topk + j] : -1;
+    }
   }
 #pragma unroll
   for (int u = 0; u < kDispU; ++u) {
@@ -161,9 +218,9 @@ __global__ __launch_bounds__(256) void k_dispatch_quant(const uint16_t* __restri
     float sc, r;
     group_scales(a, sc, r);
     const uint2 codes = cast8(f, r);
-    const int32_t* dt = dest + (int64_t)tt[u] * topk;
-    for (int j = 0; j < topk; ++j) {
-      const int32_t row = dt[j];
+    const int nk = MAXK > 0 ? MAXK : topk;
+    for (int j = 0; j < nk; ++j) {
+      const int32_t row = MAXK > 0 ? dr[u][MAXK > 0 ? j : 0] : dest[(int64_t)tt[u] * topk + j];
       if (row < 0) continue;
       store_nt8(q + (int64_t)row * ldq + kk[u] * 128u + lane16 * 8u, codes);
       if (lane16 == 0) s[(int64_t)row * s_sm + (int64_t)kk[u] * s_skb] = sc;
@@ -195,8 +252,12 @@ hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T
     const uint32_t n_tiles = (uint32_t)(T * KB);
     if (n_tiles > 0) {
       const uint32_t grid = (n_tiles + 16u * kDispU - 1) / (16u * kDispU);
-      hipLaunchKernelGGL(k_dispatch_quant, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk, dest,
-                         q, ldq, s, s_sm, s_skb);
+      if (topk <= 8)
+        hipLaunchKernelGGL(k_dispatch_quant<8>, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk,
+                           dest, q, ldq, s, s_sm, s_skb);
+      else
+        hipLaunchKernelGGL(k_dispatch_quant<0>, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk,
+                           dest, q, ldq, s, s_sm, s_skb);
     }
   }
   return hipGetLastError();

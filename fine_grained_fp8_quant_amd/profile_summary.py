@@ -23,7 +23,8 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROFILES = os.path.join(ROOT, "profiles")
-SOURCES = {"gemm": "fine_grained_fp8_quant_amd/csrc/gemm.hip", "quant": "fine_grained_fp8_quant_amd/csrc/quant.hip"}
+SOURCES = {"gemm": "fine_grained_fp8_quant_amd/csrc/gemm.hip", "quant": "fine_grained_fp8_quant_amd/csrc/quant.hip",
+           "dispatch": "fine_grained_fp8_quant_amd/csrc/dispatch.hip"}
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace/{w} -o trace -- "
              "python -u bench.py --workload {w} --steps 5 --warmup 2 --no-cpu-baseline")
@@ -54,6 +55,8 @@ def api_of(kname: str):
         return "quant_w_128x128", None
     if kname.startswith("k_fused"):
         return "fused_rmsnorm_quant", None
+    if kname.startswith("k_dispatch"):
+        return "quant_dispatch_1x128", None
     mode = "exact" if "exact" in kname else ("fp8core" if "fp8core" in kname else None)
     if kname.startswith("k_grouped"):
         return "grouped_gemm_fp8_blockscaled", mode
@@ -122,7 +125,7 @@ def summarise(out_dir, w, traffic):
                 key = f"{w}/{api}" + (f"[{md}]" if md else "")
                 sums[key][0] += rd
                 sums[key][1] += wr
-                sums[key][2] = sha(SOURCES["gemm" if "gemm" in api else "quant"])
+                sums[key][2] = sha(SOURCES["gemm" if "gemm" in api else ("dispatch" if "dispatch" in api else "quant")])
     for key, (rd, wr, src) in sums.items():
         traffic[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr, "source_sha": src}
     os.makedirs(PROFILES, exist_ok=True)

@@ -2,7 +2,8 @@
 
     rocprofv3 --pmc <counters> -- python -m fine_grained_fp8_quant_amd.profile_workload [--workload prefill]
 
-Quantises the workload's inputs, runs each GEMM mode --reps times, and runs
+Quantises (or, for the dispatch workload, quantises and dispatches) the
+workload's inputs, runs each GEMM mode --reps times, and runs
 one 1 GiB device copy (fgq_debug_copy) whose FETCH_SIZE / WRITE_SIZE
 calibrate the traffic counters (known size: 1 GiB read, 1 GiB written).
 """
@@ -17,7 +18,8 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("--workload", default="prefill", choices=["prefill", "decode", "grouped_up", "fused_down"])
+    p.add_argument("--workload", default="prefill",
+                   choices=["prefill", "decode", "grouped_up", "fused_down", "dispatch"])
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--modes", default="exact,fp8core")
     args = p.parse_args()
@@ -32,9 +34,12 @@ def main():
     d = make_workload(args.workload)
     if args.workload == "fused_down":
         fgq.fused_rmsnorm_quant(dev(d["X"]), dev(d["gamma"]), d["eps"])
-    qa, sa = fgq.quant_act_1x128(dev(d["A"]))
+    if args.workload == "dispatch":
+        qa, sa, off, _, _ = fgq.quant_dispatch_1x128(dev(d["X"]), torch.from_numpy(d["ids"]).cuda(), d["E"])
+    else:
+        qa, sa = fgq.quant_act_1x128(dev(d["A"]))
+        off = torch.from_numpy(d["offsets"]).cuda() if "offsets" in d else None
     qw, sw = fgq.quant_w_128x128(dev(d["W"]))
-    off = torch.from_numpy(d["offsets"]).cuda() if "offsets" in d else None
     for name in args.modes.split(","):
         mode = fgq.GEMM_EXACT if name == "exact" else fgq.GEMM_FP8_CORE
         for _ in range(args.reps):

@@ -150,7 +150,7 @@ WORKLOADS = {
     "fused_down": "RMSNorm(eps 1e-6, gamma U(0.5,1.5)) + quant of X [16384,7168] N(0,2); "
                   "grouped down: 32 experts, 16384 Zipf(1.1) rows, A [16384,2048] N(0,1), W [32,7168,2048] N(0,0.02)",
     "dispatch": "quantise-then-dispatch: X [4096,7168] N(0,1) tokens, top-8 of 32 experts per token "
-                "(Zipf(1.1) expert popularity) -> 32768 expert-ordered FP8 rows",
+                "(Zipf(1.1) expert popularity) -> 32768 expert-ordered FP8 rows; W [32,4096,7168] as grouped_up",
 }
 
 
@@ -229,11 +229,13 @@ def make_workload(name: str, seed: int = 0, rows: int | None = None, parts=None)
     elif name == "dispatch":
         T, topk, E, K = 4096, 8, 32, 7168
         T = T if rows is None else rows
-        d.update(T=T, topk=topk, E=E, K=K)
+        d.update(T=T, topk=topk, E=E, K=K, N=4096)
         if want("ids"):
             d["ids"] = route_ids(T, topk, E, 1.1, rng_for(seed, "ids_dispatch"))
         if want("X"):
             d["X"] = normal_bf16((T, K), 1.0, rng_for(seed, "X_dispatch"))
+        if want("W"):  # the up-projection weights of the grouped_up workload (same key)
+            d["W"] = normal_bf16((E, 4096, K), 0.02, rng_for(seed, "W_up"))
     else:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
     return d

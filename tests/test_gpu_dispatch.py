@@ -3,7 +3,7 @@
 Everything is compared bit for bit with the oracle (oracle.dispatch): the
 offsets, both index maps, and the codes and scales of every routed row.
 Cases: one pair; ragged routings with dropped and out-of-range ids; more
-than one 1024-pair routing block and a partial last block; E = 4096 (the
+than one 256-pair routing block and a partial last block; E = 4096 (the
 limit); top-1; nothing routed; T = 0; the full dispatch workload
 (4096 tokens, top-8 of 32 experts, K = 7168).  Output rows past the routed
 count keep their canary bytes, and the dispatched rows feed the grouped
@@ -56,7 +56,7 @@ def _compare(res, x, ids, E, what):
     (1, 1, 1, 128, 0.0, 0),
     (5, 2, 3, 256, 0.2, 1),
     (100, 8, 32, 384, 0.05, 2),
-    (777, 4, 5, 640, 0.0, 3),       # 3108 pairs: three full routing blocks and a partial one
+    (777, 4, 5, 640, 0.0, 3),       # 3108 pairs: twelve full 256-pair routing blocks and a partial one
     (1000, 8, 300, 128, 0.1, 4),
     (300, 6, 4096, 128, 0.0, 5),    # the largest expert count
     (3000, 1, 7, 256, 0.0, 6),
