@@ -202,5 +202,5 @@ def test_dispatch_validation(lib):
     assert dispatch(lib, ws_bytes=need - 1) == SHAPE
     assert dispatch(lib, ws=P + 65536 + 16) == ALIGN
     assert lib.fgq_quant_dispatch_workspace_bytes(0, 8, 32) == 0
-    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32) == 2 * 32 * 32 * 4
+    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32) == 2 * (4096 * 8 // 256) * 32 * 4   # 256-pair blocks
     assert lib.fgq_quant_dispatch_workspace_bytes(-1, 8, 32) == 0
