@@ -231,8 +231,13 @@ def make_step(args, fgq, d, n_sets, mode):
     return step
 
 
+CPU_TARGET_S = 10.0   # the oracle's sample grows in whole units until it has run this long
+
+
 def cpu_baseline(args, d):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole units of it (1024-row blocks of the dense GEMM, whole experts
+    largest first), added until about CPU_TARGET_S seconds have run."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -240,41 +245,48 @@ def cpu_baseline(args, d):
     except Exception:
         blas_threads = 1
     t0 = time.perf_counter()
+    flops = 0.0
     if args.workload in ("prefill", "decode"):
-        rows = min(d["M"], 4096)
-        cols = 8192 if d["M"] > 64 else d["N"]
-        qa, sa = oracle.quant_act_1x128(d["A"][:rows])
-        qw, sw = oracle.quant_w_128x128(d["W"][:cols])
-        oracle.gemm_ref(qa, sa, qw, sw)
-        flops = 2.0 * rows * cols * d["K"]
-        sample = f"A rows 0..{rows - 1} x W rows 0..{cols - 1}, full K={d['K']}: quant A, quant W, float64 GEMM"
-    elif args.workload == "dispatch":
-        offsets, row_src, _ = oracle.dispatch_ref(d["ids"], d["E"])
-        e = int(np.argmax(np.diff(offsets)))
-        rows = min(int(offsets[e + 1] - offsets[e]), 4096)
-        toks = row_src[offsets[e]:offsets[e] + rows].astype(np.int64) // d["topk"]
-        cols = d["N"]
-        ids_e = np.full((rows, 1), e, np.int32)     # the sampled rows, all routed to expert e
-        qa, sa, _, _, _ = oracle.quant_dispatch_ref(d["X"][toks], ids_e, d["E"])
-        qw, sw = oracle.quant_w_128x128(d["W"][e, :cols])
-        oracle.gemm_ref(qa, sa, qw, sw)
-        flops = 2.0 * rows * cols * d["K"]
-        sample = (f"routing of all {d['T']} tokens, then expert {e}: {rows} dispatched rows x {cols} weight rows, "
-                  f"full K={d['K']}: dispatch quant, quant W, float64 GEMM")
+        K, N, M = d["K"], d["N"], d["M"]
+        qw, sw = oracle.quant_w_128x128(d["W"])
+        rows = 0
+        while rows < M and (rows == 0 or time.perf_counter() - t0 < CPU_TARGET_S):
+            r1 = min(M, rows + 1024)
+            qa, sa = oracle.quant_act_1x128(d["A"][rows:r1])
+            oracle.gemm_ref(qa, sa, qw, sw)
+            flops += 2.0 * (r1 - rows) * N * K
+            rows = r1
+        sample = f"quant W (all {N} rows), then A rows 0..{rows - 1} of {M}: quant A, float64 GEMM against all of W"
     else:
-        e = int(np.argmax(d["counts"]))
-        r0 = int(d["offsets"][e])
-        rows = min(int(d["counts"][e]), 4096)
-        cols = d["N"]
+        K, N = d["K"], d["N"]
+        if args.workload == "dispatch":
+            offsets, row_src, _ = oracle.dispatch_ref(d["ids"], d["E"])
+            counts = np.diff(offsets)
+        else:
+            offsets, counts = d["offsets"], d["counts"]
         if args.workload == "fused_down":
-            oracle.fused_rmsnorm_quant(d["X"][:rows], d["gamma"], d["eps"])
-        qa, sa = oracle.quant_act_1x128(d["A"][r0:r0 + rows])
-        qw, sw = oracle.quant_w_128x128(d["W"][e, :cols])
-        oracle.gemm_ref(qa, sa, qw, sw)
-        flops = 2.0 * rows * cols * d["K"]
-        sample = (f"expert {e}: {rows} rows x {cols} weight rows, full K={d['K']}"
-                  + (" (+ fused RMSNorm of as many rows)" if args.workload == "fused_down" else "")
-                  + ": quant, quant W, float64 GEMM")
+            oracle.fused_rmsnorm_quant(d["X"][:1024], d["gamma"], d["eps"])
+        done = []
+        for e in np.argsort(-counts, kind="stable"):
+            if done and time.perf_counter() - t0 >= CPU_TARGET_S:
+                break
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 == r0:
+                continue
+            if args.workload == "dispatch":
+                toks = row_src[r0:r1].astype(np.int64) // d["topk"]
+                qa, sa, _, _, _ = oracle.quant_dispatch_ref(d["X"][toks], np.full((r1 - r0, 1), e, np.int32), d["E"])
+            else:
+                qa, sa = oracle.quant_act_1x128(d["A"][r0:r1])
+            qw, sw = oracle.quant_w_128x128(d["W"][e])
+            oracle.gemm_ref(qa, sa, qw, sw)
+            flops += 2.0 * (r1 - r0) * N * K
+            done.append((int(e), r1 - r0))
+        sample = (("routing of all tokens, then " if args.workload == "dispatch" else "")
+                  + ("fused RMSNorm of 1024 rows, then " if args.workload == "fused_down" else "")
+                  + f"{len(done)} experts, largest first ({sum(r for _, r in done)} rows: "
+                  + ", ".join(f"e{e}:{r}" for e, r in done) + f") x {N} weight rows, full K={K}: "
+                  + ("dispatch quant" if args.workload == "dispatch" else "quant A") + ", quant W_e, float64 GEMM")
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS",
