@@ -12,7 +12,9 @@ the BF16 inputs already resident in HBM:
     16384x2048 + quant W 32x7168x2048 + grouped down-projection GEMM;
   * dispatch: quant_dispatch_1x128 of 4096 tokens routed to 8 of 32 experts
     each (32768 expert-ordered FP8 rows) + quant W 32x4096x7168 + grouped
-    up-projection GEMM on the dispatched rows.
+    up-projection GEMM on the dispatched rows;
+  * moe_decode: the same for a 256-token decode batch (at most 256 rows per
+    expert): the grouped GEMM is bound by reading the expert weights.
 Inputs rotate over several buffer sets so the 256 MB last-level cache
 cannot serve one step from the previous one.  `value` is whole-step GEMM
 throughput: GEMM FLOPs per step / step time.  Per-kernel durations come
@@ -47,6 +49,8 @@ WORKLOAD_TITLES = {
     "grouped_up": "grouped MoE up-proj 32 experts, 32768 Zipf rows, K 7168, N 4096",
     "fused_down": "fused RMSNorm+quant 16384x7168, grouped MoE down-proj 32 experts, 16384 rows, K 2048, N 7168",
     "dispatch": "quantise-then-dispatch 4096 tokens x top-8 of 32 experts (K 7168) + grouped MoE up-proj, N 4096",
+    "moe_decode": "decode-shaped MoE: 256 tokens x top-8 of 32 experts (<= 256 rows each), dispatch + grouped "
+                  "up-proj K 7168, N 4096",
 }
 
 
@@ -116,7 +120,7 @@ def build_sets(args):
         quant_bytes = {"quant_act_1x128": 3 * R * K + 4 * R * K // 128,
                        "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
         shape = {"E": E, "rows": R, "N": N, "K": K, "counts": d["counts"].tolist()}
-    elif args.workload == "dispatch":
+    elif args.workload in ("dispatch", "moe_decode"):
         X, W = dev_bf16(d["X"]), dev_bf16(d["W"])
         T, topk, E, K, N = d["T"], d["topk"], d["E"], d["K"], d["N"]
         ids = torch.from_numpy(d["ids"]).cuda()
@@ -144,7 +148,7 @@ def build_sets(args):
         if args.workload in ("prefill", "decode", "grouped_up"):
             s["A"] = A if i == 0 else A.clone()
             s["W"] = W if i == 0 else W.clone()
-        elif args.workload == "dispatch":
+        elif args.workload in ("dispatch", "moe_decode"):
             s["X"] = X if i == 0 else X.clone()
             s["W"] = W if i == 0 else W.clone()
             s["ids"] = ids
@@ -180,7 +184,7 @@ def make_step(args, fgq, d, n_sets, mode):
             o["c"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             ws = fgq.gemm_workspace_bytes(M, N, K)
             o["ws"] = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda") if ws else None
-        elif args.workload == "dispatch":
+        elif args.workload in ("dispatch", "moe_decode"):
             T, topk, K, N, E = d["T"], d["topk"], d["K"], d["N"], d["E"]
             R = T * topk
             o["qa"] = torch.empty((R, K), dtype=torch.uint8, device="cuda")
@@ -207,7 +211,7 @@ def make_step(args, fgq, d, n_sets, mode):
 
     def step(i, s, t):
         o = outs[i]
-        if args.workload == "dispatch":
+        if args.workload in ("dispatch", "moe_decode"):
             t.run("quant_dispatch_1x128",
                   lambda: fgq.quant_dispatch_1x128(s["X"], s["ids"], d["E"], q=o["qa"], s=o["sa"], offsets=o["off"],
                                                    row_src=o["src"], dest=o["dest"], workspace=o["dws"]))
@@ -259,7 +263,7 @@ def cpu_baseline(args, d):
         sample = f"quant W (all {N} rows), then A rows 0..{rows - 1} of {M}: quant A, float64 GEMM against all of W"
     else:
         K, N = d["K"], d["N"]
-        if args.workload == "dispatch":
+        if args.workload in ("dispatch", "moe_decode"):
             offsets, row_src, _ = oracle.dispatch_ref(d["ids"], d["E"])
             counts = np.diff(offsets)
         else:
@@ -273,7 +277,7 @@ def cpu_baseline(args, d):
             r0, r1 = int(offsets[e]), int(offsets[e + 1])
             if r1 == r0:
                 continue
-            if args.workload == "dispatch":
+            if args.workload in ("dispatch", "moe_decode"):
                 toks = row_src[r0:r1].astype(np.int64) // d["topk"]
                 qa, sa, _, _, _ = oracle.quant_dispatch_ref(d["X"][toks], np.full((r1 - r0, 1), e, np.int32), d["E"])
             else:
@@ -282,11 +286,12 @@ def cpu_baseline(args, d):
             oracle.gemm_ref(qa, sa, qw, sw)
             flops += 2.0 * (r1 - r0) * N * K
             done.append((int(e), r1 - r0))
-        sample = (("routing of all tokens, then " if args.workload == "dispatch" else "")
+        sample = (("routing of all tokens, then " if args.workload in ("dispatch", "moe_decode") else "")
                   + ("fused RMSNorm of 1024 rows, then " if args.workload == "fused_down" else "")
                   + f"{len(done)} experts, largest first ({sum(r for _, r in done)} rows: "
                   + ", ".join(f"e{e}:{r}" for e, r in done) + f") x {N} weight rows, full K={K}: "
-                  + ("dispatch quant" if args.workload == "dispatch" else "quant A") + ", quant W_e, float64 GEMM")
+                  + ("dispatch quant" if args.workload in ("dispatch", "moe_decode") else "quant A")
+                  + ", quant W_e, float64 GEMM")
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS",
@@ -355,10 +360,13 @@ def main():
             kernels[k] = {"ms": ms, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
                           "algorithmic_bytes": quant_bytes[k]}
     traffic = traffic_for(f"{args.workload}/{gemm_name}[{args.mode}]")
-    if args.workload == "decode":
+    if args.workload in ("decode", "moe_decode"):
         # memory-bound: algorithmic bytes = W codes + weight scales + A codes + act scales + C
-        M, N, K = d["M"], d["N"], d["K"]
-        gbytes = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+        if args.workload == "decode":
+            M, N, K, nw = d["M"], d["N"], d["K"], 1
+        else:
+            M, N, K, nw = d["T"] * d["topk"], d["N"], d["K"], d["E"]
+        gbytes = nw * (N * K + 4 * (N // 128) * (K // 128)) + M * K + 4 * M * (K // 128) + 2 * M * N
         gbs = gbytes / (gemm_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": gemm_name, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": gbytes, "traffic": traffic}

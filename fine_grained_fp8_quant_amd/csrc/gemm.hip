@@ -382,6 +382,10 @@ using BigCfg = TileCfg<256, 256, 2, 4>;      // FP8 matrix core, large M
 using BigExactCfg = TileCfg<192, 256, 2, 4>; // exact products, large M (FP16 operands need more registers)
 using SmallCfg = TileCfg<64, 128, 1, 4>;
 using SplitCfg = TileCfg<64, 128, 1, 4, 3>;  // split-K, memory-bound small M: 3 stages, 2 per CU
+// Grouped GEMM with few rows per expert (decode batches): the expert weights
+// dominate the traffic; 128-row tiles hold most experts in one slot (one
+// pass over their weights) with three stages in flight.
+using MoeDecodeCfg = TileCfg<128, 256, 2, 4, 3>;
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict__ qa, int64_t lda,
@@ -594,6 +598,17 @@ hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, c
                                                const int32_t* offsets, int64_t E, int64_t total_rows,
                                                uint16_t* c, int64_t ldc, int64_t N, int64_t K, int mode,
                                                hipStream_t st) {
+  // decode regime: at most 128 rows per expert on average (the host decides
+  // from the sizes alone; offsets stay on the device)
+  if (total_rows <= 128 * E && N % MoeDecodeCfg::BN == 0) {
+    if (mode == 1)
+      launch_grouped<MoeDecodeCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets,
+                                      E, total_rows, c, ldc, N, K, st);
+    else
+      launch_grouped<MoeDecodeCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets,
+                                      E, total_rows, c, ldc, N, K, st);
+    return hipGetLastError();
+  }
   const bool big = N % 256 == 0 && total_rows > 128;
   if (mode == 1) {
     if (big) launch_grouped<BigCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);

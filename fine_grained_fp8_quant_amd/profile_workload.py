@@ -19,7 +19,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "grouped_up", "fused_down", "dispatch"])
+                   choices=["prefill", "decode", "grouped_up", "fused_down", "dispatch", "moe_decode"])
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--modes", default="exact,fp8core")
     args = p.parse_args()
@@ -34,7 +34,7 @@ def main():
     d = make_workload(args.workload)
     if args.workload == "fused_down":
         fgq.fused_rmsnorm_quant(dev(d["X"]), dev(d["gamma"]), d["eps"])
-    if args.workload == "dispatch":
+    if args.workload in ("dispatch", "moe_decode"):
         qa, sa, off, _, _ = fgq.quant_dispatch_1x128(dev(d["X"]), torch.from_numpy(d["ids"]).cuda(), d["E"])
     else:
         qa, sa = fgq.quant_act_1x128(dev(d["A"]))

@@ -25,6 +25,8 @@ Readings of the workload descriptions (the descriptions give no more):
     pages activate 8 routed experts per token), so it produces the 32768
     routed rows of the grouped up-projection; expert popularity follows the
     same Zipf(1.1) profile (see ``route_ids``).
+  * The decode-shaped MoE workload is the same routing for a 256-token decode
+    batch, so every expert gets at most 256 rows (the pages' decode regime).
 """
 from __future__ import annotations
 
@@ -151,6 +153,8 @@ WORKLOADS = {
                   "grouped down: 32 experts, 16384 Zipf(1.1) rows, A [16384,2048] N(0,1), W [32,7168,2048] N(0,0.02)",
     "dispatch": "quantise-then-dispatch: X [4096,7168] N(0,1) tokens, top-8 of 32 experts per token "
                 "(Zipf(1.1) expert popularity) -> 32768 expert-ordered FP8 rows; W [32,4096,7168] as grouped_up",
+    "moe_decode": "decode-shaped MoE up-projection: 256 tokens, top-8 of 32 experts (at most 256 rows per expert), "
+                  "dispatched, grouped GEMM against W [32,4096,7168] as grouped_up",
 }
 
 
@@ -226,8 +230,8 @@ def make_workload(name: str, seed: int = 0, rows: int | None = None, parts=None)
             d["A"] = normal_bf16((R, K), 1.0, rng_for(seed, "A_down"))
         if want("W"):
             d["W"] = normal_bf16((E, N, K), 0.02, rng_for(seed, "W_down"))
-    elif name == "dispatch":
-        T, topk, E, K = 4096, 8, 32, 7168
+    elif name in ("dispatch", "moe_decode"):
+        T, topk, E, K = (4096 if name == "dispatch" else 256), 8, 32, 7168
         T = T if rows is None else rows
         d.update(T=T, topk=topk, E=E, K=K, N=4096)
         if want("ids"):

@@ -306,3 +306,29 @@ def test_grouped_full_size_sampled(fgq_gpu, name, mode):
         ref = oracle.gemm_ref(qao, sao, qwo, swo)
         _check(host_bf16_f64(c[rows.tolist()]), ref, f"{name} full, expert {e} ({r1 - r0} rows)", mode,
                qao, sao, qwo, swo)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_grouped_moe_decode_full_size(fgq_gpu, mode):
+    """Decode-shaped MoE (256 tokens, top-8 of 32 experts, at most 256 rows per
+    expert) dispatched and multiplied on the GPU, as the benchmark runs it;
+    every row of three experts (the largest, a small one, the last) is checked
+    against the oracle's own dispatch, quantisation and product."""
+    import torch
+    d = make_workload("moe_decode")
+    X, W, ids, E = d["X"], d["W"], d["ids"], d["E"]
+    qa, sa, off, _, _ = fgq_gpu.quant_dispatch_1x128(dev_bf16(X), torch.from_numpy(ids).cuda(), E)
+    qw, sw = fgq_gpu.quant_w_128x128(dev_bf16(W))
+    c = fgq_gpu.grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, off, mode=mode)
+    torch.cuda.synchronize()
+    offo, srco, _ = oracle.dispatch_ref(ids, E)
+    assert np.array_equal(off.cpu().numpy(), offo)
+    counts = np.diff(offo)
+    nz = np.nonzero(counts)[0]
+    for e in sorted({int(np.argmax(counts)), int(nz[np.argmin(counts[nz])]), int(nz[-1])}):
+        r0, r1 = int(offo[e]), int(offo[e + 1])
+        toks = srco[r0:r1].astype(np.int64) // d["topk"]
+        qao, sao = oracle.quant_act_1x128(X[toks])
+        qwo, swo = oracle.quant_w_128x128(W[e])
+        ref = oracle.gemm_ref(qao, sao, qwo, swo)
+        _check(host_bf16_f64(c[r0:r1]), ref, f"moe_decode expert {e} ({r1 - r0} rows)", mode, qao, sao, qwo, swo)
