@@ -66,3 +66,12 @@ from .dispatch import (  # noqa: F401
     dispatch_ref,
     quant_dispatch_ref,
 )
+from .e8m0 import (  # noqa: F401
+    e8m0_decode,
+    e8m0_exponent,
+    fused_rmsnorm_quant_e8m0,
+    gemm_e8m0_ref,
+    grouped_gemm_e8m0_ref,
+    quant_act_1x128_e8m0,
+    quant_w_128x128_e8m0,
+)
