@@ -15,6 +15,9 @@ the BF16 inputs already resident in HBM:
     up-projection GEMM on the dispatched rows;
   * moe_decode: the same for a 256-token decode batch (at most 256 rows per
     expert): the grouped GEMM is bound by reading the expert weights.
+With --scales e8m0 every step uses the power-of-two scale variant (E8M0
+scale bytes, applied by the FP8 matrix core); --mode then picks how the GEMM
+accumulates (promote: per-chunk FP32 promotion; incore: in the matrix core).
 Inputs rotate over several buffer sets so the 256 MB last-level cache
 cannot serve one step from the previous one.  `value` is whole-step GEMM
 throughput: GEMM FLOPs per step / step time.  Per-kernel durations come
@@ -63,9 +66,18 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 768 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--mode", default="exact", choices=["exact", "fp8core"],
-                   help="GEMM accumulation: exact products (FP16 matrix cores) or FP8 matrix cores")
-    return p.parse_args()
+    p.add_argument("--scales", default="f32", choices=["f32", "e8m0"],
+                   help="scale format: binary32 (a/448) or power-of-two E8M0 bytes")
+    p.add_argument("--mode", default=None, choices=["exact", "fp8core", "promote", "incore"],
+                   help="GEMM accumulation. f32 scales: exact products (FP16 matrix cores, default) or FP8 "
+                        "matrix cores; e8m0 scales: promote (default) or incore")
+    args = p.parse_args()
+    modes = {"f32": ("exact", "fp8core"), "e8m0": ("promote", "incore")}[args.scales]
+    if args.mode is None:
+        args.mode = modes[0]
+    if args.mode not in modes:
+        p.error(f"--mode {args.mode} does not apply to --scales {args.scales} (use {' or '.join(modes)})")
+    return args
 
 
 def sha(path):
@@ -103,13 +115,14 @@ def build_sets(args):
     from synth import make_workload
     d = make_workload(args.workload, seed=args.seed)
     sets = []
+    sb = 1 if args.scales == "e8m0" else 4      # bytes per stored scale
     if args.workload in ("prefill", "decode"):
         A, W = dev_bf16(d["A"]), dev_bf16(d["W"])
         M, K, N = d["M"], d["K"], d["N"]
         per_set = (A.numel() * 3 + W.numel() * 3 + M * N * 2)
         flops = 2.0 * M * N * K
-        quant_bytes = {"quant_act_1x128": 3 * M * K + 4 * M * K // 128,
-                       "quant_w_128x128": 3 * N * K + 4 * N * K // 16384}
+        quant_bytes = {"quant_act_1x128": 3 * M * K + sb * M * K // 128,
+                       "quant_w_128x128": 3 * N * K + sb * N * K // 16384}
         shape = {"M": M, "N": N, "K": K}
     elif args.workload == "grouped_up":
         A, W = dev_bf16(d["A"]), dev_bf16(d["W"])
@@ -117,8 +130,8 @@ def build_sets(args):
         off = torch.from_numpy(d["offsets"]).cuda()
         per_set = A.numel() * 3 + W.numel() * 3 + R * N * 2
         flops = 2.0 * R * N * K
-        quant_bytes = {"quant_act_1x128": 3 * R * K + 4 * R * K // 128,
-                       "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
+        quant_bytes = {"quant_act_1x128": 3 * R * K + sb * R * K // 128,
+                       "quant_w_128x128": 3 * E * N * K + sb * E * N * K // 16384}
         shape = {"E": E, "rows": R, "N": N, "K": K, "counts": d["counts"].tolist()}
     elif args.workload in ("dispatch", "moe_decode"):
         X, W = dev_bf16(d["X"]), dev_bf16(d["W"])
@@ -127,8 +140,8 @@ def build_sets(args):
         R = T * topk
         per_set = X.numel() * 2 + R * K + W.numel() * 3 + R * N * 2
         flops = 2.0 * R * N * K
-        quant_bytes = {"quant_dispatch_1x128": 2 * T * K + R * K + 4 * R * K // 128 + 4 * R + 4 * (E + 1) + 8 * R,
-                       "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
+        quant_bytes = {"quant_dispatch_1x128": 2 * T * K + R * K + sb * R * K // 128 + 4 * R + 4 * (E + 1) + 8 * R,
+                       "quant_w_128x128": 3 * E * N * K + sb * E * N * K // 16384}
         shape = {"tokens": T, "topk": topk, "E": E, "rows": R, "N": N, "K": K}
     else:
         X, G = dev_bf16(d["X"]), dev_bf16(d["gamma"])
@@ -138,10 +151,12 @@ def build_sets(args):
         off = torch.from_numpy(d["offsets"]).cuda()
         per_set = X.numel() * 3 + A.numel() * 3 + W.numel() * 3 + R * N * 2
         flops = 2.0 * R * N * K
-        quant_bytes = {"fused_rmsnorm_quant": 3 * Mx * Kx + 4 * Mx * Kx // 128 + 2 * Kx,
-                       "quant_act_1x128": 3 * R * K + 4 * R * K // 128,
-                       "quant_w_128x128": 3 * E * N * K + 4 * E * N * K // 16384}
+        quant_bytes = {"fused_rmsnorm_quant": 3 * Mx * Kx + sb * Mx * Kx // 128 + 2 * Kx,
+                       "quant_act_1x128": 3 * R * K + sb * R * K // 128,
+                       "quant_w_128x128": 3 * E * N * K + sb * E * N * K // 16384}
         shape = {"Mx": Mx, "Kx": Kx, "E": E, "rows": R, "N": N, "K": K, "counts": d["counts"].tolist()}
+    if args.scales == "e8m0":
+        quant_bytes = {k + "_e8m0": v for k, v in quant_bytes.items()}
     n_sets = args.sets or max(2, int(np.ceil(768e6 / per_set)))
     for i in range(n_sets):
         s = {}
@@ -164,13 +179,39 @@ def build_sets(args):
 
 
 def gemm_mode(fgq, name):
-    return fgq.GEMM_EXACT if name == "exact" else fgq.GEMM_FP8_CORE
+    return {"exact": fgq.GEMM_EXACT, "fp8core": fgq.GEMM_FP8_CORE, "promote": fgq.E8M0_PROMOTE,
+            "incore": fgq.E8M0_IN_CORE}[name]
+
+
+class Api:
+    """The calls of one scale format under the names the step times them by."""
+
+    def __init__(self, fgq, scales):
+        import torch
+        e8 = scales == "e8m0"
+        sfx = "_e8m0" if e8 else ""
+        self.sdtype = torch.uint8 if e8 else torch.float32
+        self.names = {n: n + sfx for n in ("quant_act_1x128", "quant_w_128x128", "fused_rmsnorm_quant",
+                                           "quant_dispatch_1x128")}
+        self.names["gemm"] = "gemm_fp8_e8m0" if e8 else "gemm_fp8_blockscaled"
+        self.names["grouped"] = "grouped_gemm_fp8_e8m0" if e8 else "grouped_gemm_fp8_blockscaled"
+        self.quant_act = getattr(fgq, self.names["quant_act_1x128"])
+        self.quant_w = getattr(fgq, self.names["quant_w_128x128"])
+        self.fused = getattr(fgq, self.names["fused_rmsnorm_quant"])
+        self.dispatch = getattr(fgq, self.names["quant_dispatch_1x128"])
+        gemm, grouped = getattr(fgq, self.names["gemm"]), getattr(fgq, self.names["grouped"])
+        kw = "accumulate" if e8 else "mode"
+        self.gemm = lambda *a, mode, **k: gemm(*a, **{kw: mode}, **k)
+        self.grouped = lambda *a, mode, **k: grouped(*a, **{kw: mode}, **k)
 
 
 def make_step(args, fgq, d, n_sets, mode):
     """Allocates every output buffer up front; returns step(i, set, timer)
     running the whole path once on input set i."""
     import torch
+    api = Api(fgq, args.scales)
+    nm = api.names
+    sdt = api.sdtype
     eps = d.get("eps", 0.0)
     outs = []
     for _ in range(n_sets):
@@ -178,9 +219,9 @@ def make_step(args, fgq, d, n_sets, mode):
         if args.workload in ("prefill", "decode"):
             M, K, N = d["M"], d["K"], d["N"]
             o["qa"] = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-            o["sa"] = fgq.act_scales(M, K, "cuda")
+            o["sa"] = fgq.act_scales(M, K, "cuda", sdt)
             o["qw"] = torch.empty((N, K), dtype=torch.uint8, device="cuda")
-            o["sw"] = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+            o["sw"] = torch.empty((N // 128, K // 128), dtype=sdt, device="cuda")
             o["c"] = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             ws = fgq.gemm_workspace_bytes(M, N, K)
             o["ws"] = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda") if ws else None
@@ -188,50 +229,47 @@ def make_step(args, fgq, d, n_sets, mode):
             T, topk, K, N, E = d["T"], d["topk"], d["K"], d["N"], d["E"]
             R = T * topk
             o["qa"] = torch.empty((R, K), dtype=torch.uint8, device="cuda")
-            o["sa"] = fgq.act_scales(R, K, "cuda")
+            o["sa"] = fgq.act_scales(R, K, "cuda", sdt)
             o["off"] = torch.empty(E + 1, dtype=torch.int32, device="cuda")
             o["src"] = torch.empty(R, dtype=torch.int32, device="cuda")
             o["dest"] = torch.empty(R, dtype=torch.int32, device="cuda")
             o["dws"] = torch.empty(max(fgq.quant_dispatch_workspace_bytes(T, topk, E), 1), dtype=torch.uint8,
                                    device="cuda")
             o["qw"] = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
-            o["sw"] = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda")
+            o["sw"] = torch.empty((E, N // 128, K // 128), dtype=sdt, device="cuda")
             o["c"] = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
         else:
             R, K, N, E = d["R"], d["K"], d["N"], d["E"]
             if args.workload == "fused_down":
                 o["qx"] = torch.empty((d["Mx"], d["Kx"]), dtype=torch.uint8, device="cuda")
-                o["sx"] = fgq.act_scales(d["Mx"], d["Kx"], "cuda")
+                o["sx"] = fgq.act_scales(d["Mx"], d["Kx"], "cuda", sdt)
             o["qa"] = torch.empty((R, K), dtype=torch.uint8, device="cuda")
-            o["sa"] = fgq.act_scales(R, K, "cuda")
+            o["sa"] = fgq.act_scales(R, K, "cuda", sdt)
             o["qw"] = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
-            o["sw"] = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda")
+            o["sw"] = torch.empty((E, N // 128, K // 128), dtype=sdt, device="cuda")
             o["c"] = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
         outs.append(o)
 
     def step(i, s, t):
         o = outs[i]
         if args.workload in ("dispatch", "moe_decode"):
-            t.run("quant_dispatch_1x128",
-                  lambda: fgq.quant_dispatch_1x128(s["X"], s["ids"], d["E"], q=o["qa"], s=o["sa"], offsets=o["off"],
-                                                   row_src=o["src"], dest=o["dest"], workspace=o["dws"]))
-            t.run("quant_w_128x128", lambda: fgq.quant_w_128x128(s["W"], q=o["qw"], s=o["sw"]))
-            t.run("grouped_gemm_fp8_blockscaled",
-                  lambda: fgq.grouped_gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], o["off"],
-                                                           out=o["c"], mode=mode))
+            t.run(nm["quant_dispatch_1x128"],
+                  lambda: api.dispatch(s["X"], s["ids"], d["E"], q=o["qa"], s=o["sa"], offsets=o["off"],
+                                       row_src=o["src"], dest=o["dest"], workspace=o["dws"]))
+            t.run(nm["quant_w_128x128"], lambda: api.quant_w(s["W"], q=o["qw"], s=o["sw"]))
+            t.run(nm["grouped"], lambda: api.grouped(o["qa"], o["sa"], o["qw"], o["sw"], o["off"], out=o["c"],
+                                                     mode=mode))
             return
         if args.workload == "fused_down":
-            t.run("fused_rmsnorm_quant", lambda: fgq.fused_rmsnorm_quant(s["X"], s["G"], eps, q=o["qx"], s=o["sx"]))
-        t.run("quant_act_1x128", lambda: fgq.quant_act_1x128(s["A"], q=o["qa"], s=o["sa"]))
-        t.run("quant_w_128x128", lambda: fgq.quant_w_128x128(s["W"], q=o["qw"], s=o["sw"]))
+            t.run(nm["fused_rmsnorm_quant"], lambda: api.fused(s["X"], s["G"], eps, q=o["qx"], s=o["sx"]))
+        t.run(nm["quant_act_1x128"], lambda: api.quant_act(s["A"], q=o["qa"], s=o["sa"]))
+        t.run(nm["quant_w_128x128"], lambda: api.quant_w(s["W"], q=o["qw"], s=o["sw"]))
         if args.workload in ("prefill", "decode"):
-            t.run("gemm_fp8_blockscaled",
-                  lambda: fgq.gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"],
-                                                   workspace=o["ws"], mode=mode))
+            t.run(nm["gemm"], lambda: api.gemm(o["qa"], o["sa"], o["qw"], o["sw"], out=o["c"], workspace=o["ws"],
+                                               mode=mode))
         else:
-            t.run("grouped_gemm_fp8_blockscaled",
-                  lambda: fgq.grouped_gemm_fp8_blockscaled(o["qa"], o["sa"], o["qw"], o["sw"], s["off"],
-                                                           out=o["c"], mode=mode))
+            t.run(nm["grouped"], lambda: api.grouped(o["qa"], o["sa"], o["qw"], o["sw"], s["off"], out=o["c"],
+                                                     mode=mode))
     return step
 
 
@@ -243,6 +281,12 @@ def cpu_baseline(args, d):
     whole units of it (1024-row blocks of the dense GEMM, whole experts
     largest first), added until about CPU_TARGET_S seconds have run."""
     import oracle
+    e8 = args.scales == "e8m0"
+    q_act = oracle.quant_act_1x128_e8m0 if e8 else oracle.quant_act_1x128
+    q_w = oracle.quant_w_128x128_e8m0 if e8 else oracle.quant_w_128x128
+    gemm_ref = oracle.gemm_e8m0_ref if e8 else oracle.gemm_ref
+    q_disp = oracle.quant_dispatch_e8m0_ref if e8 else oracle.quant_dispatch_ref
+    fused = oracle.fused_rmsnorm_quant_e8m0 if e8 else oracle.fused_rmsnorm_quant
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
@@ -252,12 +296,12 @@ def cpu_baseline(args, d):
     flops = 0.0
     if args.workload in ("prefill", "decode"):
         K, N, M = d["K"], d["N"], d["M"]
-        qw, sw = oracle.quant_w_128x128(d["W"])
+        qw, sw = q_w(d["W"])
         rows = 0
         while rows < M and (rows == 0 or time.perf_counter() - t0 < CPU_TARGET_S):
             r1 = min(M, rows + 1024)
-            qa, sa = oracle.quant_act_1x128(d["A"][rows:r1])
-            oracle.gemm_ref(qa, sa, qw, sw)
+            qa, sa = q_act(d["A"][rows:r1])
+            gemm_ref(qa, sa, qw, sw)
             flops += 2.0 * (r1 - rows) * N * K
             rows = r1
         sample = f"quant W (all {N} rows), then A rows 0..{rows - 1} of {M}: quant A, float64 GEMM against all of W"
@@ -269,7 +313,7 @@ def cpu_baseline(args, d):
         else:
             offsets, counts = d["offsets"], d["counts"]
         if args.workload == "fused_down":
-            oracle.fused_rmsnorm_quant(d["X"][:1024], d["gamma"], d["eps"])
+            fused(d["X"][:1024], d["gamma"], d["eps"])
         done = []
         for e in np.argsort(-counts, kind="stable"):
             if done and time.perf_counter() - t0 >= CPU_TARGET_S:
@@ -279,11 +323,11 @@ def cpu_baseline(args, d):
                 continue
             if args.workload in ("dispatch", "moe_decode"):
                 toks = row_src[r0:r1].astype(np.int64) // d["topk"]
-                qa, sa, _, _, _ = oracle.quant_dispatch_ref(d["X"][toks], np.full((r1 - r0, 1), e, np.int32), d["E"])
+                qa, sa, _, _, _ = q_disp(d["X"][toks], np.full((r1 - r0, 1), e, np.int32), d["E"])
             else:
-                qa, sa = oracle.quant_act_1x128(d["A"][r0:r1])
-            qw, sw = oracle.quant_w_128x128(d["W"][e])
-            oracle.gemm_ref(qa, sa, qw, sw)
+                qa, sa = q_act(d["A"][r0:r1])
+            qw, sw = q_w(d["W"][e])
+            gemm_ref(qa, sa, qw, sw)
             flops += 2.0 * (r1 - r0) * N * K
             done.append((int(e), r1 - r0))
         sample = (("routing of all tokens, then " if args.workload in ("dispatch", "moe_decode") else "")
@@ -294,7 +338,8 @@ def cpu_baseline(args, d):
                   + ", quant W_e, float64 GEMM")
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS",
+            "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS"
+                      + ("; E8M0 scales" if e8 else ""),
             "seconds": dt}
 
 
@@ -349,7 +394,7 @@ def main():
     gemm_name = [k for k in kern if "gemm" in k][0]
     gemm_ms = kern[gemm_name]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
-    peak = PEAK_FP16_TFLOPS if args.mode == "exact" else PEAK_FP8_TFLOPS
+    peak = PEAK_FP16_TFLOPS if args.mode == "exact" else PEAK_FP8_TFLOPS   # e8m0 modes run on the FP8 cores
     kernels = {}
     for k, ms in kern.items():
         if "gemm" in k:
@@ -366,7 +411,8 @@ def main():
             M, N, K, nw = d["M"], d["N"], d["K"], 1
         else:
             M, N, K, nw = d["T"] * d["topk"], d["N"], d["K"], d["E"]
-        gbytes = nw * (N * K + 4 * (N // 128) * (K // 128)) + M * K + 4 * M * (K // 128) + 2 * M * N
+        sb = 1 if args.scales == "e8m0" else 4
+        gbytes = nw * (N * K + sb * (N // 128) * (K // 128)) + M * K + sb * M * (K // 128) + 2 * M * N
         gbs = gbytes / (gemm_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": gemm_name, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": gbytes, "traffic": traffic}
@@ -378,7 +424,7 @@ def main():
                     "traffic": traffic}
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
     # the other GEMM accumulation mode, timed alone (not part of the step)
-    other = "fp8core" if args.mode == "exact" else "exact"
+    other = {"exact": "fp8core", "fp8core": "exact", "promote": "incore", "incore": "promote"}[args.mode]
     alt_step = make_step(args, fgq, d, len(sets), gemm_mode(fgq, other))
     alt_t = Timer()
     for i in range(max(3, args.steps // 2)):
@@ -403,10 +449,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "e4m3 codes; " + ("products on fp16 matrix cores (exact)" if args.mode == "exact"
-                                   else "fp8 matrix cores") + "; fp32 accumulate",
+                                   else "fp8 matrix cores") + "; "
+                 + {"exact": "fp32 scales, fp32 accumulate", "fp8core": "fp32 scales, fp32 accumulate",
+                    "promote": "e8m0 scales applied by the unit, fp32 accumulate",
+                    "incore": "e8m0 scales applied by the unit, accumulate in the matrix core"}[args.mode],
         "data": "synthetic (seeded, shapes and distributions of the named workload)",
         "config": {"workload": WORKLOAD_TITLES[args.workload], **{k: v for k, v in shape.items() if k != "counts"},
-                   "input_sets": len(sets)},
+                   "scales": args.scales, "input_sets": len(sets)},
         "roofline": roofline,
         "kernels": kernels,
         "gemm_mode": args.mode,

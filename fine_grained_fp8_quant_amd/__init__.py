@@ -14,6 +14,14 @@ Functions (same names as the C ABI in include/fgq.h, without the prefix):
     grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets) -> c bfloat16 [R, N]
     quant_dispatch_1x128(x, ids, E)        -> (q, s, offsets, row_src, dest): FP8 rows grouped by expert
 
+Power-of-two (E8M0) scale variants, scales as uint8 exponent bytes
+(value = 2^(byte - 127)) that the FP8 matrix core applies itself:
+
+    quant_act_1x128_e8m0(x), quant_w_128x128_e8m0(w), fused_rmsnorm_quant_e8m0(x, gamma, eps)
+    quant_dispatch_1x128_e8m0(x, ids, E)
+    gemm_fp8_e8m0(qa, sa, qw, sw, accumulate=E8M0_PROMOTE)
+    grouped_gemm_fp8_e8m0(qa, sa, qw, sw, offsets, accumulate=E8M0_PROMOTE)
+
 Codes are returned as ``torch.uint8`` (``.view(torch.float8_e4m3fn)`` gives
 the FP8 dtype).  Scales may be any strided float32 view; the strides are
 passed to the kernels as they are.  Activation scales are allocated
@@ -32,12 +40,18 @@ __all__ = [
     "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled", "gemm_workspace_bytes",
     "quant_dispatch_1x128", "quant_dispatch_workspace_bytes",
     "debug_encode_e4m3", "debug_copy", "debug_mfma_16x16x128", "STATUS", "GEMM_EXACT", "GEMM_FP8_CORE",
+    "quant_act_1x128_e8m0", "quant_w_128x128_e8m0", "fused_rmsnorm_quant_e8m0", "act_scales_e8m0",
+    "gemm_fp8_e8m0", "grouped_gemm_fp8_e8m0", "debug_mfma_e8m0_16x16x128", "E8M0_PROMOTE", "E8M0_IN_CORE",
+    "quant_dispatch_1x128_e8m0",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 
 GEMM_EXACT = 0       # exact FP8 products on the FP16 matrix cores (default)
 GEMM_FP8_CORE = 1    # FP8 matrix cores: 2x rate, ~13-bit in-group accumulation window
+
+E8M0_PROMOTE = 0     # E8M0 GEMMs: per-chunk sum promoted into an FP32 accumulator (default)
+E8M0_IN_CORE = 1     # E8M0 GEMMs: running sum kept in the matrix core (no promotion)
 
 STATUS = {
     0: "FGQ_OK", 1: "FGQ_ERR_NULL", 2: "FGQ_ERR_SHAPE", 3: "FGQ_ERR_ALIGN",
@@ -80,6 +94,16 @@ _SIGNATURES = {
     "fgq_debug_encode_e4m3": [ctypes.c_uint32, _i64, _vp, _vp],
     "fgq_debug_copy": [_vp, _vp, _i64, _vp],
     "fgq_debug_mfma_16x16x128": [_vp, _vp, _vp, _vp, _vp],
+    "fgq_quant_act_1x128_e8m0": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp],
+    "fgq_quant_w_128x128_e8m0": [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp],
+    "fgq_fused_rmsnorm_quant_e8m0": [_vp, _i64, _vp, _f32, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp],
+    "fgq_gemm_fp8_e8m0": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
+                          _i64, _i64, _i64, _st, _vp, ctypes.c_size_t, _vp],
+    "fgq_grouped_gemm_fp8_e8m0": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                  _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _st, _vp],
+    "fgq_debug_mfma_e8m0_16x16x128": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "fgq_quant_dispatch_1x128_e8m0": [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                                      _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
 }
 _RESTYPES = {
     "fgq_gemm_workspace_bytes": ctypes.c_size_t,
@@ -143,10 +167,11 @@ def _need(t, dtype, what):
         raise ValueError(f"{what}: the last dimension must be contiguous")
 
 
-def _need_scales(t, what):
+def _need_scales(t, what, dtype=None):
     torch = _torch()
-    if t.dtype != torch.float32:
-        raise TypeError(f"{what}: expected float32 scales, got {t.dtype}")
+    dtype = torch.float32 if dtype is None else dtype
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype} scales, got {t.dtype}")
     if t.numel() > 0 and not t.is_cuda:
         raise ValueError(f"{what}: expected a device tensor")
 
@@ -159,17 +184,20 @@ def _codes(t):
     return t
 
 
-def act_scales(M: int, K: int, device):
-    """Uninitialised activation-scale buffer for an [M, K] operand: a float32
-    [M, K/128] view of K-block-major storage (strides (1, M))."""
+def act_scales(M: int, K: int, device, dtype=None):
+    """Uninitialised activation-scale buffer for an [M, K] operand: a
+    [M, K/128] view of K-block-major storage (strides (1, M)); float32 unless
+    ``dtype`` says otherwise."""
     torch = _torch()
-    return torch.empty((K // 128, M), dtype=torch.float32, device=device).t()
+    return torch.empty((K // 128, M), dtype=dtype or torch.float32, device=device).t()
 
 
-def quant_act_1x128(x, q=None, s=None, stream=None):
-    """1x128 tile quantisation of BF16 ``x [M, K]``.  Optional preallocated
-    outputs ``q`` (uint8 [M, K]) and ``s`` (float32 view of shape [M, K/128],
-    any strides)."""
+def act_scales_e8m0(M: int, K: int, device):
+    """As act_scales, for E8M0 exponent bytes (uint8)."""
+    return act_scales(M, K, device, _torch().uint8)
+
+
+def _quant_act(fn, sdtype, x, q, s, stream):
     torch = _torch()
     load_library()
     _need(x, torch.bfloat16, "x")
@@ -177,14 +205,27 @@ def quant_act_1x128(x, q=None, s=None, stream=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if s is None:
-        s = act_scales(M, K, x.device)
-    _check(lib.fgq_quant_act_1x128(_ptr(x), x.stride(0), M, K, _ptr(q), q.stride(0), _ptr(s),
-                                   s.stride(0), s.stride(1), _stream(stream)))
+        s = act_scales(M, K, x.device, sdtype)
+    _need_scales(s, "s", sdtype)
+    _check(fn(_ptr(x), x.stride(0), M, K, _ptr(q), q.stride(0), _ptr(s), s.stride(0), s.stride(1), _stream(stream)))
     return q, s
 
 
-def quant_w_128x128(w, q=None, s=None, stream=None):
-    """128x128 block quantisation of BF16 ``w [N, K]`` or ``[B, N, K]``."""
+def quant_act_1x128(x, q=None, s=None, stream=None):
+    """1x128 tile quantisation of BF16 ``x [M, K]``.  Optional preallocated
+    outputs ``q`` (uint8 [M, K]) and ``s`` (float32 view of shape [M, K/128],
+    any strides)."""
+    load_library()
+    return _quant_act(lib.fgq_quant_act_1x128, _torch().float32, x, q, s, stream)
+
+
+def quant_act_1x128_e8m0(x, q=None, s=None, stream=None):
+    """quant_act_1x128 with power-of-two scales: ``s`` holds uint8 E8M0 bytes."""
+    load_library()
+    return _quant_act(lib.fgq_quant_act_1x128_e8m0, _torch().uint8, x, q, s, stream)
+
+
+def _quant_w(fn, sdtype, w, q, s, stream):
     torch = _torch()
     load_library()
     _need(w, torch.bfloat16, "w")
@@ -196,17 +237,28 @@ def quant_w_128x128(w, q=None, s=None, stream=None):
     elif not batched:
         q = q.unsqueeze(0)
     if s is None:
-        s = torch.empty((B, N // 128, K // 128), dtype=torch.float32, device=w.device)
+        s = torch.empty((B, N // 128, K // 128), dtype=sdtype, device=w.device)
     elif not batched:
         s = s.unsqueeze(0)
-    _check(lib.fgq_quant_w_128x128(_ptr(w3), w3.stride(1), w3.stride(0), B, N, K, _ptr(q), q.stride(1),
-                                   q.stride(0), _ptr(s), s.stride(1), s.stride(2), s.stride(0),
-                                   _stream(stream)))
+    _need_scales(s, "s", sdtype)
+    _check(fn(_ptr(w3), w3.stride(1), w3.stride(0), B, N, K, _ptr(q), q.stride(1), q.stride(0), _ptr(s),
+              s.stride(1), s.stride(2), s.stride(0), _stream(stream)))
     return (q, s) if batched else (q[0], s[0])
 
 
-def fused_rmsnorm_quant(x, gamma, eps: float, q=None, s=None, stream=None):
-    """RMSNorm(x; gamma, eps) in binary32 fused with 1x128 quantisation."""
+def quant_w_128x128(w, q=None, s=None, stream=None):
+    """128x128 block quantisation of BF16 ``w [N, K]`` or ``[B, N, K]``."""
+    load_library()
+    return _quant_w(lib.fgq_quant_w_128x128, _torch().float32, w, q, s, stream)
+
+
+def quant_w_128x128_e8m0(w, q=None, s=None, stream=None):
+    """quant_w_128x128 with power-of-two scales: ``s`` holds uint8 E8M0 bytes."""
+    load_library()
+    return _quant_w(lib.fgq_quant_w_128x128_e8m0, _torch().uint8, w, q, s, stream)
+
+
+def _fused(fn, sdtype, x, gamma, eps, q, s, stream):
     torch = _torch()
     load_library()
     _need(x, torch.bfloat16, "x")
@@ -217,10 +269,23 @@ def fused_rmsnorm_quant(x, gamma, eps: float, q=None, s=None, stream=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if s is None:
-        s = act_scales(M, K, x.device)
-    _check(lib.fgq_fused_rmsnorm_quant(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(q),
-                                       q.stride(0), _ptr(s), s.stride(0), s.stride(1), _stream(stream)))
+        s = act_scales(M, K, x.device, sdtype)
+    _need_scales(s, "s", sdtype)
+    _check(fn(_ptr(x), x.stride(0), _ptr(gamma), float(eps), M, K, _ptr(q), q.stride(0), _ptr(s), s.stride(0),
+              s.stride(1), _stream(stream)))
     return q, s
+
+
+def fused_rmsnorm_quant(x, gamma, eps: float, q=None, s=None, stream=None):
+    """RMSNorm(x; gamma, eps) in binary32 fused with 1x128 quantisation."""
+    load_library()
+    return _fused(lib.fgq_fused_rmsnorm_quant, _torch().float32, x, gamma, eps, q, s, stream)
+
+
+def fused_rmsnorm_quant_e8m0(x, gamma, eps: float, q=None, s=None, stream=None):
+    """fused_rmsnorm_quant with power-of-two scales (uint8 E8M0 bytes)."""
+    load_library()
+    return _fused(lib.fgq_fused_rmsnorm_quant_e8m0, _torch().uint8, x, gamma, eps, q, s, stream)
 
 
 def quant_dispatch_workspace_bytes(T: int, topk: int, E: int) -> int:
@@ -236,8 +301,21 @@ def quant_dispatch_1x128(x, ids, n_experts: int, q=None, s=None, offsets=None, r
     room for ``T * topk`` rows (rows of expert e are
     ``offsets[e] .. offsets[e+1] - 1``), ``offsets`` int32 ``[E + 1]``,
     ``row_src`` and ``dest`` int32 ``[T * topk]`` (see include/fgq.h)."""
-    torch = _torch()
     load_library()
+    return _dispatch(lib.fgq_quant_dispatch_1x128, _torch().float32, x, ids, n_experts, q, s, offsets, row_src,
+                     dest, workspace, stream)
+
+
+def quant_dispatch_1x128_e8m0(x, ids, n_experts: int, q=None, s=None, offsets=None, row_src=None, dest=None,
+                              workspace=None, stream=None):
+    """quant_dispatch_1x128 with power-of-two scales (``s`` uint8 E8M0 bytes)."""
+    load_library()
+    return _dispatch(lib.fgq_quant_dispatch_1x128_e8m0, _torch().uint8, x, ids, n_experts, q, s, offsets, row_src,
+                     dest, workspace, stream)
+
+
+def _dispatch(fn, sdtype, x, ids, n_experts, q, s, offsets, row_src, dest, workspace, stream):
+    torch = _torch()
     _need(x, torch.bfloat16, "x")
     _need(ids, torch.int32, "ids")
     T, K = x.shape
@@ -249,7 +327,8 @@ def quant_dispatch_1x128(x, ids, n_experts: int, q=None, s=None, offsets=None, r
     if q is None:
         q = torch.empty((R, K), dtype=torch.uint8, device=dev)
     if s is None:
-        s = act_scales(R, K, dev)
+        s = act_scales(R, K, dev, sdtype)
+    _need_scales(s, "s", sdtype)
     if offsets is None:
         offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
     if row_src is None:
@@ -260,9 +339,8 @@ def quant_dispatch_1x128(x, ids, n_experts: int, q=None, s=None, offsets=None, r
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.fgq_quant_dispatch_1x128(_ptr(x), x.stride(0), T, K, _ptr(ids), topk, n_experts, _ptr(q),
-                                        q.stride(0), _ptr(s), s.stride(0), s.stride(1), _ptr(offsets),
-                                        _ptr(row_src), _ptr(dest), _ptr(workspace), ws_bytes, _stream(stream)))
+    _check(fn(_ptr(x), x.stride(0), T, K, _ptr(ids), topk, n_experts, _ptr(q), q.stride(0), _ptr(s), s.stride(0),
+              s.stride(1), _ptr(offsets), _ptr(row_src), _ptr(dest), _ptr(workspace), ws_bytes, _stream(stream)))
     return q, s, offsets, row_src, dest
 
 
@@ -274,13 +352,25 @@ def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 def gemm_fp8_blockscaled(qa, sa, qw, sw, out=None, workspace=None, mode=GEMM_EXACT, stream=None):
     """``C = (dec(qa) * sa) @ (dec(qw) * sw).T`` with per-chunk FP32 promotion, BF16 out.
     ``mode``: GEMM_EXACT (default) or GEMM_FP8_CORE."""
-    torch = _torch()
     load_library()
+    return _gemm(lib.fgq_gemm_fp8_blockscaled, _torch().float32, qa, sa, qw, sw, out, workspace, mode, stream)
+
+
+def gemm_fp8_e8m0(qa, sa, qw, sw, out=None, workspace=None, accumulate=E8M0_PROMOTE, stream=None):
+    """The block-scaled GEMM with E8M0 scale bytes ``sa`` [M, K/128] and ``sw``
+    [N/128, K/128] (uint8), applied by the matrix core.  ``accumulate``:
+    E8M0_PROMOTE (default) or E8M0_IN_CORE."""
+    load_library()
+    return _gemm(lib.fgq_gemm_fp8_e8m0, _torch().uint8, qa, sa, qw, sw, out, workspace, accumulate, stream)
+
+
+def _gemm(fn, sdtype, qa, sa, qw, sw, out, workspace, mode, stream):
+    torch = _torch()
     qa, qw = _codes(qa), _codes(qw)
     _need(qa, torch.uint8, "qa")
     _need(qw, torch.uint8, "qw")
-    _need_scales(sa, "sa")
-    _need_scales(sw, "sw")
+    _need_scales(sa, "sa", sdtype)
+    _need_scales(sw, "sw", sdtype)
     M, K = qa.shape
     N = qw.shape[0]
     if qw.shape[1] != K:
@@ -291,24 +381,36 @@ def gemm_fp8_blockscaled(qa, sa, qw, sw, out=None, workspace=None, mode=GEMM_EXA
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qa.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
-    _check(lib.fgq_gemm_fp8_blockscaled(_ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1),
-                                        _ptr(qw), qw.stride(0), _ptr(sw), sw.stride(0), sw.stride(1),
-                                        _ptr(out), out.stride(0), M, N, K, int(mode), _ptr(workspace),
-                                        ws_bytes, _stream(stream)))
+    _check(fn(_ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(0), _ptr(sw),
+              sw.stride(0), sw.stride(1), _ptr(out), out.stride(0), M, N, K, int(mode), _ptr(workspace), ws_bytes,
+              _stream(stream)))
     return out
 
 
 def grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets, out=None, mode=GEMM_EXACT, stream=None):
     """Ragged grouped GEMM: rows ``offsets[e]..offsets[e+1]`` of ``qa`` times expert
     ``e``'s ``qw[e]``.  ``offsets`` is a device int32 tensor of E+1 entries."""
-    torch = _torch()
     load_library()
+    return _grouped(lib.fgq_grouped_gemm_fp8_blockscaled, _torch().float32, qa, sa, qw, sw, offsets, out, mode,
+                    stream)
+
+
+def grouped_gemm_fp8_e8m0(qa, sa, qw, sw, offsets, out=None, accumulate=E8M0_PROMOTE, stream=None):
+    """grouped_gemm_fp8_blockscaled with E8M0 scale bytes (uint8) and the
+    accumulation choice of gemm_fp8_e8m0."""
+    load_library()
+    return _grouped(lib.fgq_grouped_gemm_fp8_e8m0, _torch().uint8, qa, sa, qw, sw, offsets, out, accumulate,
+                    stream)
+
+
+def _grouped(fn, sdtype, qa, sa, qw, sw, offsets, out, mode, stream):
+    torch = _torch()
     qa, qw = _codes(qa), _codes(qw)
     _need(qa, torch.uint8, "qa")
     _need(qw, torch.uint8, "qw")
     _need(offsets, torch.int32, "offsets")
-    _need_scales(sa, "sa")
-    _need_scales(sw, "sw")
+    _need_scales(sa, "sa", sdtype)
+    _need_scales(sw, "sw", sdtype)
     R, K = qa.shape
     E, N, K2 = qw.shape
     if K2 != K:
@@ -317,10 +419,9 @@ def grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets, out=None, mode=GEMM_EX
         raise ValueError("offsets must have E + 1 entries")
     if out is None:
         out = torch.empty((R, N), dtype=torch.bfloat16, device=qa.device)
-    _check(lib.fgq_grouped_gemm_fp8_blockscaled(
-        _ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(1),
-        qw.stride(0), _ptr(sw), sw.stride(1), sw.stride(2), sw.stride(0), _ptr(offsets), E, R,
-        _ptr(out), out.stride(0), N, K, int(mode), _stream(stream)))
+    _check(fn(_ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(1), qw.stride(0),
+              _ptr(sw), sw.stride(1), sw.stride(2), sw.stride(0), _ptr(offsets), E, R, _ptr(out), out.stride(0), N, K,
+              int(mode), _stream(stream)))
     return out
 
 
@@ -343,6 +444,19 @@ def debug_mfma_16x16x128(a, b, cin=None, stream=None):
     d = torch.empty((16, 16), dtype=torch.float32, device=a.device)
     _check(lib.fgq_debug_mfma_16x16x128(_ptr(a.contiguous()), _ptr(b.contiguous()), _ptr(cin.contiguous()),
                                         _ptr(d), _stream(stream)))
+    return d
+
+
+def debug_mfma_e8m0_16x16x128(a, b, sa, sb, cin=None, stream=None):
+    """One scaled matrix-core op: a, b uint8 E4M3 [16,128]; sa, sb uint8 [16] E8M0
+    row / column scales; returns float32 [16,16] = diag(2^(sa-127)) a b^T diag(2^(sb-127)) + cin."""
+    torch = _torch()
+    load_library()
+    if cin is None:
+        cin = torch.zeros((16, 16), dtype=torch.float32, device=a.device)
+    d = torch.empty((16, 16), dtype=torch.float32, device=a.device)
+    _check(lib.fgq_debug_mfma_e8m0_16x16x128(_ptr(a.contiguous()), _ptr(b.contiguous()), _ptr(sa.contiguous()),
+                                             _ptr(sb.contiguous()), _ptr(cin.contiguous()), _ptr(d), _stream(stream)))
     return d
 
 

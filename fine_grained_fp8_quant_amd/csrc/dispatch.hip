@@ -186,11 +186,11 @@ constexpr int kDispU = 4;
 
 // MAXK > 0: topk <= MAXK, the destination rows of each tile's token are
 // loaded with the tile (no dependent load before each store); MAXK = 0: any topk.
-template <int MAXK>
+template <class SF, int MAXK>
 __global__ __launch_bounds__(256) void k_dispatch_quant(const uint16_t* __restrict__ x, int64_t ldx, uint32_t KB,
                                                         uint32_t n_tiles, int topk, const int32_t* __restrict__ dest,
-                                                        uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
-                                                        int64_t s_sm, int64_t s_skb) {
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        typename SF::T* __restrict__ s, int64_t s_sm, int64_t s_skb) {
   const uint32_t lane16 = threadIdx.x & 15u;
   const uint32_t grp = threadIdx.x >> 4;
   const uint32_t first = blockIdx.x * (16u * kDispU) + grp;
@@ -215,8 +215,9 @@ __global__ __launch_bounds__(256) void k_dispatch_quant(const uint16_t* __restri
     float f[8];
     unpack8(v[u], f);
     const float a = max16(absmax8(f));
-    float sc, r;
-    group_scales(a, sc, r);
+    typename SF::T sc;
+    float r;
+    SF::derive(a, sc, r);
     const uint2 codes = cast8(f, r);
     const int nk = MAXK > 0 ? MAXK : topk;
     for (int j = 0; j < nk; ++j) {
@@ -235,10 +236,11 @@ size_t dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
   return (size_t)(2 * nb * E) * sizeof(int32_t);
 }
 
-hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
-                                       const int32_t* ids, int64_t topk, int64_t E, uint8_t* q, int64_t ldq,
-                                       float* s, int64_t s_sm, int64_t s_skb, int32_t* offsets,
-                                       int32_t* row_src, int32_t* dest, void* workspace, hipStream_t st) {
+template <class SF>
+static hipError_t launch_dispatch(const uint16_t* x, int64_t ldx, int64_t T, int64_t K, const int32_t* ids,
+                                  int64_t topk, int64_t E, uint8_t* q, int64_t ldq, typename SF::T* s, int64_t s_sm,
+                                  int64_t s_skb, int32_t* offsets, int32_t* row_src, int32_t* dest, void* workspace,
+                                  hipStream_t st) {
   const int64_t N = T * topk;
   const int nb = (int)((N + kPairsPerBlock - 1) / kPairsPerBlock);
   int32_t* counts = static_cast<int32_t*>(workspace);
@@ -253,14 +255,30 @@ hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T
     if (n_tiles > 0) {
       const uint32_t grid = (n_tiles + 16u * kDispU - 1) / (16u * kDispU);
       if (topk <= 8)
-        hipLaunchKernelGGL(k_dispatch_quant<8>, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk,
+        hipLaunchKernelGGL((k_dispatch_quant<SF, 8>), dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk,
                            dest, q, ldq, s, s_sm, s_skb);
       else
-        hipLaunchKernelGGL(k_dispatch_quant<0>, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk,
+        hipLaunchKernelGGL((k_dispatch_quant<SF, 0>), dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, (int)topk,
                            dest, q, ldq, s, s_sm, s_skb);
     }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                       const int32_t* ids, int64_t topk, int64_t E, uint8_t* q, int64_t ldq,
+                                       float* s, int64_t s_sm, int64_t s_skb, int32_t* offsets,
+                                       int32_t* row_src, int32_t* dest, void* workspace, hipStream_t st) {
+  return launch_dispatch<ScaleF32>(x, ldx, T, K, ids, topk, E, q, ldq, s, s_sm, s_skb, offsets, row_src, dest,
+                                   workspace, st);
+}
+
+hipError_t launch_quant_dispatch_1x128_e8m0(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                            const int32_t* ids, int64_t topk, int64_t E, uint8_t* q, int64_t ldq,
+                                            uint8_t* s, int64_t s_sm, int64_t s_skb, int32_t* offsets,
+                                            int32_t* row_src, int32_t* dest, void* workspace, hipStream_t st) {
+  return launch_dispatch<ScaleE8M0>(x, ldx, T, K, ids, topk, E, q, ldq, s, s_sm, s_skb, offsets, row_src, dest,
+                                    workspace, st);
 }
 
 }  // namespace fgq

@@ -71,6 +71,31 @@ __device__ __forceinline__ void group_scales(float a, float& s, float& r) {
   r = fminf(kE4M3Max / a, kFltMax);
 }
 
+// Power-of-two scale of a group from its max-abs a (finite, >= 0): the
+// smallest 2^e with 448 * 2^e >= a, e >= -127, as the E8M0 byte e + 127, and
+// the exact cast multiplier r = 2^-e.  With a = f * 2^E (1 <= f < 2) and
+// 448 = 1.75 * 2^8, e = E - 8 when f <= 1.75 and E - 7 otherwise; f > 1.75 is
+// a mantissa field above 0x600000.  Zero and subnormal a give byte 0 (their
+// true e is below -127).  Bytes stay <= 247 for finite a, so 2^-e is normal.
+__device__ __forceinline__ void group_scales_e8m0(float a, uint8_t& byte, float& r) {
+  const uint32_t u = __float_as_uint(a);
+  int b = (int)(u >> 23) - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  b = b < 0 ? 0 : b;
+  byte = (uint8_t)b;
+  r = __uint_as_float((uint32_t)(254 - b) << 23);  // 2^(127 - b)
+}
+
+// Scale formats of the quantisers: the stored scale type and its derivation
+// from the group max-abs (stored scale s, cast multiplier r).
+struct ScaleF32 {
+  using T = float;
+  static __device__ __forceinline__ void derive(float a, T& s, float& r) { group_scales(a, s, r); }
+};
+struct ScaleE8M0 {
+  using T = uint8_t;
+  static __device__ __forceinline__ void derive(float a, T& s, float& r) { group_scales_e8m0(a, s, r); }
+};
+
 // Eight binary32 values times r, clamped and encoded; returns 8 codes.
 __device__ __forceinline__ uint2 cast8(const float* f, float r) {
   uint2 o;

@@ -42,8 +42,38 @@ hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T
 
 size_t dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E);
 
+// Power-of-two (E8M0 byte) scale variants of the quantisers and GEMMs.
+hipError_t launch_quant_act_1x128_e8m0(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                       int64_t ldq, uint8_t* s, int64_t s_sm, int64_t s_skb, hipStream_t st);
+
+hipError_t launch_quant_w_128x128_e8m0(const uint16_t* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N,
+                                       int64_t K, uint8_t* q, int64_t ldq, int64_t q_bs, uint8_t* s,
+                                       int64_t s_snb, int64_t s_skb, int64_t s_bs, hipStream_t st);
+
+hipError_t launch_fused_rmsnorm_quant_e8m0(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                                           int64_t M, int64_t K, uint8_t* q, int64_t ldq, uint8_t* s,
+                                           int64_t s_sm, int64_t s_skb, hipStream_t st);
+
+hipError_t launch_quant_dispatch_1x128_e8m0(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                            const int32_t* ids, int64_t topk, int64_t E, uint8_t* q, int64_t ldq,
+                                            uint8_t* s, int64_t s_sm, int64_t s_skb, int32_t* offsets,
+                                            int32_t* row_src, int32_t* dest, void* workspace, hipStream_t st);
+
+hipError_t launch_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm, int64_t sa_skb,
+                                const uint8_t* qw, int64_t ldw, const uint8_t* sw, int64_t sw_snb, int64_t sw_skb,
+                                uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int in_core,
+                                void* workspace, size_t workspace_bytes, hipStream_t st);
+
+hipError_t launch_grouped_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm,
+                                        int64_t sa_skb, const uint8_t* qw, int64_t ldw, int64_t w_es,
+                                        const uint8_t* sw, int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+                                        const int32_t* offsets, int64_t E, int64_t total_rows, uint16_t* c,
+                                        int64_t ldc, int64_t N, int64_t K, int in_core, hipStream_t st);
+
 hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_debug_mfma(const uint8_t* a, const uint8_t* b, const float* cin, float* d, hipStream_t st);
+hipError_t launch_debug_mfma_e8m0(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                 const float* cin, float* d, hipStream_t st);
 
 }  // namespace fgq

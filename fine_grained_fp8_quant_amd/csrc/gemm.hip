@@ -37,6 +37,22 @@
 //     per-chunk activation scales are one 4-byte load per row; stored
 //     K-block-major ([K/128][M]) they are contiguous, which is the layout the
 //     quantisers' callers should prefer.
+//   * Power-of-two (E8M0) scales, the microscaling block-scale format the
+//     pages relate the method to (P1 paragraph 4, P4 paragraph 3): the FP8
+//     matrix core applies them itself (v_mfma_scale_f32_16x16x128_f8f6f4,
+//     one byte per lane = per row of A or column of B and 32-value K block;
+//     every lane of a row gets the same byte, as the block is 128 wide).
+//     Two ways to accumulate: promote (each chunk into a zero C, then an
+//     FP32 add on the vector ALU, the pages' promotion), or in the matrix
+//     core (C = the running sum, no vector work).  Measured: the unit aligns
+//     C and the chunk's 8-product group sums to the largest of them and
+//     truncates about 24 bits below it, so keeping the sum in the matrix
+//     core costs at most ~2^-20 of it per chunk, unlike the ~14 bits the
+//     pages report for H800.
+//     Scale bytes travel in the same 4-byte DMA slots as binary32 scales
+//     (the aligned word holding the byte) and are read back as single bytes.
+#include <type_traits>
+
 #include "fgq_device.h"
 #include "fgq_launch.h"
 
@@ -56,6 +72,26 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// The same with E8M0 block scales (byte 127 = 1.0): D = 2^(sa - 127) *
+// 2^(sb - 127) * A B^T + C, sa from the lane's row of A, sb from the lane's
+// column of B.  With C = 0 the result is the unscaled one times the two
+// powers of two, exactly.  C and the scaled group sums are added in a window
+// about 24 bits below the largest of them (truncating below it).
+__device__ __forceinline__ v4f mfma_16x16x128_fp8_e8m0(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Scale element type of a mode: binary32 for exact (0) and FP8 core (1),
+// E8M0 bytes for the scaled matrix-core modes (2: promote, 3: in-core).
+template <int MODE>
+using ScaleOf = typename std::conditional<(MODE >= 2), uint8_t, float>::type;
+
+// Aligned 32-bit word that holds the scale at p (the DMA moves words).
+template <class S>
+__device__ __forceinline__ const void* word_of(const S* p) {
+  return reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)3);
 }
 
 // 16x16 output, K = 32 FP16.  Products of E4M3 values are exact in it and
@@ -130,14 +166,20 @@ __device__ __forceinline__ int lds_col(int c, int r) { return c ^ ((r >> 1) & 7)
 // accumulators; chunk() multiplies the K chunk staged at `base` (layout of
 // TileCfg) into them and store() writes the wave's part of the tile.
 
-// 16x16 sub-tiles: FP8 matrix core (MODE 1), or exact products as four
-// K = 32 steps on the FP16 matrix core (MODE 0).  Lane (l16, lgrp) feeds row
-// l16 of a sub-tile with code bytes 32 lgrp ... 32 lgrp + 31 of the chunk.
+// 16x16 sub-tiles: FP8 matrix core (MODE 1), exact products as four K = 32
+// steps on the FP16 matrix core (MODE 0), or the FP8 matrix core with E8M0
+// scales applied by the unit (MODE 2 promote, MODE 3 in-core).  Lane
+// (l16, lgrp) feeds row l16 of a sub-tile with code bytes 32 lgrp ...
+// 32 lgrp + 31 of the chunk.
 template <class C, int MODE>
 struct Engine16 {
   v4f acc[C::TM][C::TN];
   int wm, wn, l16, lgrp;
   int a_off0, a_off1, b_off0, b_off1, sa_off, sw_idx;
+  // E8M0 modes: low address bits of this lane's A scale and the wave's
+  // weight scale at chunk 0, and the per-chunk strides; the byte sits at
+  // (address mod 4) inside its DMA slot.
+  uint32_t sa_lo = 0, sa_step = 0, sw_lo = 0, sw_step = 0;
 
   __device__ __forceinline__ Engine16(int wave, int lane) {
     wm = wave / C::WAVES_N;
@@ -157,11 +199,90 @@ struct Engine16 {
     a_off1 = (wm * C::WM + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
     b_off0 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0, l16) << 4);
     b_off1 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
-    sa_off = C::SA_OFF + (wm * C::WM + lgrp * 4) * 4;
+    sa_off = MODE >= 2 ? C::SA_OFF + (wm * C::WM + l16) * 4 : C::SA_OFF + (wm * C::WM + lgrp * 4) * 4;
     sw_idx = (wn * C::WN) / 128;
   }
 
-  __device__ __forceinline__ void chunk(const uint8_t* base) {
+  __device__ __forceinline__ void chunk(const uint8_t* base, int kb) {
+    if constexpr (MODE >= 2) chunk_e8m0(base, kb);
+    else chunk_f32(base);
+  }
+
+  // E8M0: one scale byte per sub-tile row (this lane's row l16) and one per
+  // wave for the weights; the unit multiplies them in
+  __device__ __forceinline__ void chunk_e8m0(const uint8_t* base, int kb) {
+    const int swv = base[C::SW_OFF + sw_idx * 4 + ((sw_lo + (uint32_t)kb * sw_step) & 3u)];
+    const int a_byte = sa_off + (int)((sa_lo + (uint32_t)kb * sa_step) & 3u);
+    v8i bf[C::TN];
+#pragma unroll
+    for (int ni = 0; ni < C::TN; ++ni) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + b_off0 + ni * 2048);
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + b_off1 + ni * 2048);
+      bf[ni] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
+    uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
+    int sav = base[a_byte];
+    // promote: the chunk sums of sub-tile row mi are added one row later,
+    // after the next row's operations are issued, so no add waits on the
+    // operation that produces its input
+    v4f tp[C::TN];
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi) {
+      uint4 nlo = alo, nhi = ahi;
+      int nsa = sav;
+      if (mi + 1 < C::TM) {
+        nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+        nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+        nsa = base[a_byte + (mi + 1) * 64];
+      }
+      const v8i af = (v8i){(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+      if constexpr (MODE == 2) {
+        v4f tc[C::TN];
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni)
+          tc[ni] = mfma_16x16x128_fp8_e8m0(af, bf[ni], (v4f){0.0f, 0.0f, 0.0f, 0.0f}, sav, swv);
+        // keep this order: the scheduler would otherwise pull the adds up
+        // against the operations that produce them
+        __builtin_amdgcn_sched_barrier(0);
+        if (mi > 0) {
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) add4(acc[mi - 1][ni], tp[ni]);
+        }
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) tp[ni] = tc[ni];
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) acc[mi][ni] = mfma_16x16x128_fp8_e8m0(af, bf[ni], acc[mi][ni], sav, swv);
+      }
+      alo = nlo;
+      ahi = nhi;
+      sav = nsa;
+    }
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) add4(acc[C::TM - 1][ni], tp[ni]);
+    }
+  }
+
+  // a += t * s elementwise, four binary32 fused multiply-adds
+  static __device__ __forceinline__ void fma4(v4f& a, const v4f& t, const v4f& s) {
+    a[0] = __builtin_fmaf(t[0], s[0], a[0]);
+    a[1] = __builtin_fmaf(t[1], s[1], a[1]);
+    a[2] = __builtin_fmaf(t[2], s[2], a[2]);
+    a[3] = __builtin_fmaf(t[3], s[3], a[3]);
+  }
+
+  // four binary32 adds (no packed instructions)
+  static __device__ __forceinline__ void add4(v4f& a, const v4f& t) {
+    a[0] += t[0];
+    a[1] += t[1];
+    a[2] += t[2];
+    a[3] += t[3];
+  }
+
+  // binary32 scales: the chunk's FP32 sum, then promotion by the vector ALU
+  __device__ __forceinline__ void chunk_f32(const uint8_t* base) {
     const float swv = reinterpret_cast<const float*>(base + C::SW_OFF)[sw_idx];
     if constexpr (MODE == 1) {
       // FP8 matrix core: one instruction per 16x16 sub-tile and chunk
@@ -172,10 +293,13 @@ struct Engine16 {
         const uint4 hi = *reinterpret_cast<const uint4*>(base + b_off1 + ni * 2048);
         bf[ni] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-      // A codes and scales one sub-tile row ahead
+      // A codes and scales one sub-tile row ahead; the chunk sums of row mi
+      // are promoted one row later, after row mi + 1's operations are issued
       uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
       uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
       v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
+      v4f tp[C::TN];
+      v4f sp;
 #pragma unroll
       for (int mi = 0; mi < C::TM; ++mi) {
         uint4 nlo = alo, nhi = ahi;
@@ -186,19 +310,24 @@ struct Engine16 {
           nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
         }
         const v8i af = (v8i){(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
-        const float s0 = sa4[0] * swv, s1 = sa4[1] * swv, s2 = sa4[2] * swv, s3 = sa4[3] * swv;
+        v4f tc[C::TN];
 #pragma unroll
-        for (int ni = 0; ni < C::TN; ++ni) {
-          const v4f t = mfma_16x16x128_fp8(af, bf[ni]);
-          acc[mi][ni][0] = __builtin_fmaf(t[0], s0, acc[mi][ni][0]);
-          acc[mi][ni][1] = __builtin_fmaf(t[1], s1, acc[mi][ni][1]);
-          acc[mi][ni][2] = __builtin_fmaf(t[2], s2, acc[mi][ni][2]);
-          acc[mi][ni][3] = __builtin_fmaf(t[3], s3, acc[mi][ni][3]);
+        for (int ni = 0; ni < C::TN; ++ni) tc[ni] = mfma_16x16x128_fp8(af, bf[ni]);
+        __builtin_amdgcn_sched_barrier(0);  // as in chunk_e8m0: keep the promotion behind them
+        if (mi > 0) {
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) fma4(acc[mi - 1][ni], tp[ni], sp);
         }
+        const v4f sc = {sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv};
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) tp[ni] = tc[ni];
+        sp = sc;
         alo = nlo;
         ahi = nhi;
         sa4 = nsa;
       }
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[C::TM - 1][ni], tp[ni], sp);
     } else {
       // exact products: codes -> FP16 in registers, four K = 32 steps per chunk
       v8h bh[C::TN][4];
@@ -280,10 +409,10 @@ struct Engine16 {
 // binary32 sums of its chunks to part[m * ldc + n] (split-K workspace).
 template <class C, int MODE, bool PARTIAL = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_t lda,
-                                          const float* __restrict__ sa, int64_t sa_sm, int64_t sa_skb,
+                                          const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm, int64_t sa_skb,
                                           int64_t row_begin, int64_t row_end,
                                           const uint8_t* __restrict__ qw, int64_t ldw,
-                                          const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
+                                          const ScaleOf<MODE>* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
                                           int64_t n0, uint16_t* __restrict__ c, float* __restrict__ part,
                                           int64_t ldc, int kb_begin, int kb_end, uint8_t* lds) {
   const int tid = threadIdx.x;
@@ -313,7 +442,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
     const int r = (wave + j * C::NW) * 8 + (lane >> 3);
     b_src[j] = (uint32_t)((r < C::BN ? r : 0) * ldw) + dcol;
   }
-  const float* s_src = nullptr;  // activation scales (waves < SA_INS) or weight scales (wave SA_INS)
+  const ScaleOf<MODE>* s_src = nullptr;  // activation scales (waves < SA_INS) or weight scales (wave SA_INS)
   if (wave < C::SA_INS) {
     int64_t gr = row_begin + wave * 64 + lane;
     gr = gr < row_end ? gr : row_end - 1;
@@ -331,15 +460,24 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
 #pragma unroll
     for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
     if (wave < C::SA_INS) {
-      dma4(s_src + (int64_t)kb * sa_skb, base + C::SA_OFF + wave * 256);
+      dma4(word_of(s_src + (int64_t)kb * sa_skb), base + C::SA_OFF + wave * 256);
     } else if (wave == C::SA_INS) {
-      if (lane < C::NBW) dma4(s_src + (int64_t)kb * sw_skb, base + C::SW_OFF);
+      if (lane < C::NBW) dma4(word_of(s_src + (int64_t)kb * sw_skb), base + C::SW_OFF);
     } else if (lane == 0) {
-      dma4(sw, base + C::SW_OFF + 128);  // dummy: keeps the per-wave DMA count uniform
+      dma4(word_of(sw), base + C::SW_OFF + 128);  // dummy: keeps the per-wave DMA count uniform
     }
   };
 
   Engine16<C, MODE> eng(wave, lane);
+  if constexpr (MODE >= 2) {
+    // slot r of the A scales holds the word of tile row r (clamped rows are
+    // never stored, so their byte offset does not matter)
+    const int64_t ar = row_begin + eng.wm * C::WM + eng.l16;
+    eng.sa_lo = (uint32_t)reinterpret_cast<uintptr_t>(sa) + (uint32_t)(ar * sa_sm);
+    eng.sa_step = (uint32_t)sa_skb;
+    eng.sw_lo = (uint32_t)reinterpret_cast<uintptr_t>(sw) + (uint32_t)(((n0 >> 7) + eng.sw_idx) * sw_snb);
+    eng.sw_step = (uint32_t)sw_skb;
+  }
 
   // NSTAGE-deep pipeline: chunk kb + NSTAGE - 1 is requested while chunk kb
   // is multiplied.  At the top of iteration kb, the wait leaves the chunks
@@ -355,7 +493,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
     barrier_no_drain();
     if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-    eng.chunk(lds + stage * C::STAGE);
+    eng.chunk(lds + stage * C::STAGE, kb);
   }
   eng.template store<PARTIAL>(row_begin, row_end, n0, c, part, ldc);
 }
@@ -389,9 +527,9 @@ using MoeDecodeCfg = TileCfg<128, 256, 2, 4, 3>;
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict__ qa, int64_t lda,
-                                                       const float* __restrict__ sa, int64_t sa_sm,
+                                                       const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
                                                        int64_t sa_skb, const uint8_t* __restrict__ qw,
-                                                       int64_t ldw, const float* __restrict__ sw,
+                                                       int64_t ldw, const ScaleOf<MODE>* __restrict__ sw,
                                                        int64_t sw_snb, int64_t sw_skb,
                                                        uint16_t* __restrict__ c, int64_t ldc, int64_t M,
                                                        int tiles_m, int KB) {
@@ -406,9 +544,9 @@ __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict
 // chunks [split * KB / S, (split + 1) * KB / S) into part[split][M][N].
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs_splitk(const uint8_t* __restrict__ qa, int64_t lda,
-                                                              const float* __restrict__ sa, int64_t sa_sm,
+                                                              const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
                                                               int64_t sa_skb, const uint8_t* __restrict__ qw,
-                                                              int64_t ldw, const float* __restrict__ sw,
+                                                              int64_t ldw, const ScaleOf<MODE>* __restrict__ sw,
                                                               int64_t sw_snb, int64_t sw_skb,
                                                               float* __restrict__ part, int64_t M, int64_t N,
                                                               int tiles_m, int tiles, int KB, int S) {
@@ -475,8 +613,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 template <class C, int MODE>
-static void launch_dense(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm, int64_t sa_skb,
-                         const uint8_t* qw, int64_t ldw, const float* sw, int64_t sw_snb, int64_t sw_skb,
+static void launch_dense(const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa, int64_t sa_sm, int64_t sa_skb,
+                         const uint8_t* qw, int64_t ldw, const ScaleOf<MODE>* sw, int64_t sw_snb, int64_t sw_skb,
                          uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int tiles_m = (int)((M + C::BM - 1) / C::BM);
   const int tiles_n = (int)(N / C::BN);
@@ -485,8 +623,8 @@ static void launch_dense(const uint8_t* qa, int64_t lda, const float* sa, int64_
 }
 
 template <int MODE>
-static void launch_splitk(const SplitPlan& p, const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
-                          int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw, int64_t sw_snb,
+static void launch_splitk(const SplitPlan& p, const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa, int64_t sa_sm,
+                          int64_t sa_skb, const uint8_t* qw, int64_t ldw, const ScaleOf<MODE>* sw, int64_t sw_snb,
                           int64_t sw_skb, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                           float* part, hipStream_t st) {
   using C = SplitCfg;
@@ -498,24 +636,41 @@ static void launch_splitk(const SplitPlan& p, const uint8_t* qa, int64_t lda, co
                      c, ldc);
 }
 
+// Large-M tile of a mode: FP16 operands (exact mode) need more registers.
+template <int MODE>
+using BigOf = typename std::conditional<MODE == 0, BigExactCfg, BigCfg>::type;
+
+template <int MODE>
+static hipError_t gemm_dispatch(const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa, int64_t sa_sm,
+                                int64_t sa_skb, const uint8_t* qw, int64_t ldw, const ScaleOf<MODE>* sw,
+                                int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
+                                int64_t K, void* workspace, hipStream_t st) {
+  const SplitPlan p = split_plan(M, N, K);
+  float* part = static_cast<float*>(workspace);
+  const bool big = M > 128 && N % 256 == 0;
+  if (p.S > 1) launch_splitk<MODE>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
+  else if (big) launch_dense<BigOf<MODE>, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+  else launch_dense<SmallCfg, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                        int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw,
                                        int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc,
                                        int64_t M, int64_t N, int64_t K, int mode, void* workspace, size_t,
                                        hipStream_t st) {
-  const SplitPlan p = split_plan(M, N, K);
-  float* part = static_cast<float*>(workspace);
-  const bool big = M > 128 && N % 256 == 0;
-  if (mode == 1) {
-    if (p.S > 1) launch_splitk<1>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
-    else if (big) launch_dense<BigCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
-    else launch_dense<SmallCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
-  } else {
-    if (p.S > 1) launch_splitk<0>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
-    else if (big) launch_dense<BigExactCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
-    else launch_dense<SmallCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
-  }
-  return hipGetLastError();
+  if (mode == 1)
+    return gemm_dispatch<1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
+  return gemm_dispatch<0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
+}
+
+hipError_t launch_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm, int64_t sa_skb,
+                                const uint8_t* qw, int64_t ldw, const uint8_t* sw, int64_t sw_snb, int64_t sw_skb,
+                                uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int in_core,
+                                void* workspace, size_t, hipStream_t st) {
+  if (in_core)
+    return gemm_dispatch<3>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
+  return gemm_dispatch<2>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -526,9 +681,9 @@ hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const flo
 // never reads the routing result.  Slots past the last real tile leave at once.
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
-    const uint8_t* __restrict__ qa, int64_t lda, const float* __restrict__ sa, int64_t sa_sm,
+    const uint8_t* __restrict__ qa, int64_t lda, const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
     int64_t sa_skb, const uint8_t* __restrict__ qw, int64_t ldw, int64_t w_es,
-    const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+    const ScaleOf<MODE>* __restrict__ sw, int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
     const int32_t* __restrict__ offsets, int E, int64_t total_rows, uint16_t* __restrict__ c,
     int64_t ldc, int slots, int KB) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
@@ -578,8 +733,8 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
 }
 
 template <class C, int MODE>
-static void launch_grouped(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm, int64_t sa_skb,
-                           const uint8_t* qw, int64_t ldw, int64_t w_es, const float* sw, int64_t sw_snb,
+static void launch_grouped(const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa, int64_t sa_sm, int64_t sa_skb,
+                           const uint8_t* qw, int64_t ldw, int64_t w_es, const ScaleOf<MODE>* sw, int64_t sw_snb,
                            int64_t sw_skb, int64_t sw_es, const int32_t* offsets, int64_t E,
                            int64_t total_rows, uint16_t* c, int64_t ldc, int64_t N, int64_t K, hipStream_t st) {
   // each non-empty expert adds at most one partial m-tile
@@ -591,6 +746,26 @@ static void launch_grouped(const uint8_t* qa, int64_t lda, const float* sa, int6
                      ldc, slots, (int)(K / 128));
 }
 
+template <int MODE>
+static hipError_t grouped_dispatch(const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa, int64_t sa_sm,
+                                   int64_t sa_skb, const uint8_t* qw, int64_t ldw, int64_t w_es,
+                                   const ScaleOf<MODE>* sw, int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+                                   const int32_t* offsets, int64_t E, int64_t total_rows, uint16_t* c, int64_t ldc,
+                                   int64_t N, int64_t K, hipStream_t st) {
+  // decode regime: at most 128 rows per expert on average (the host decides
+  // from the sizes alone; offsets stay on the device)
+  if (total_rows <= 128 * E && N % MoeDecodeCfg::BN == 0)
+    launch_grouped<MoeDecodeCfg, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets,
+                                       E, total_rows, c, ldc, N, K, st);
+  else if (N % 256 == 0 && total_rows > 128)
+    launch_grouped<BigOf<MODE>, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets,
+                                      E, total_rows, c, ldc, N, K, st);
+  else
+    launch_grouped<SmallCfg, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E,
+                                   total_rows, c, ldc, N, K, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa,
                                                int64_t sa_sm, int64_t sa_skb, const uint8_t* qw,
                                                int64_t ldw, int64_t w_es, const float* sw,
@@ -598,26 +773,23 @@ hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, c
                                                const int32_t* offsets, int64_t E, int64_t total_rows,
                                                uint16_t* c, int64_t ldc, int64_t N, int64_t K, int mode,
                                                hipStream_t st) {
-  // decode regime: at most 128 rows per expert on average (the host decides
-  // from the sizes alone; offsets stay on the device)
-  if (total_rows <= 128 * E && N % MoeDecodeCfg::BN == 0) {
-    if (mode == 1)
-      launch_grouped<MoeDecodeCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets,
-                                      E, total_rows, c, ldc, N, K, st);
-    else
-      launch_grouped<MoeDecodeCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets,
-                                      E, total_rows, c, ldc, N, K, st);
-    return hipGetLastError();
-  }
-  const bool big = N % 256 == 0 && total_rows > 128;
-  if (mode == 1) {
-    if (big) launch_grouped<BigCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
-    else launch_grouped<SmallCfg, 1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
-  } else {
-    if (big) launch_grouped<BigExactCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
-    else launch_grouped<SmallCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, c, ldc, N, K, st);
-  }
-  return hipGetLastError();
+  if (mode == 1)
+    return grouped_dispatch<1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E,
+                               total_rows, c, ldc, N, K, st);
+  return grouped_dispatch<0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E,
+                             total_rows, c, ldc, N, K, st);
+}
+
+hipError_t launch_grouped_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm,
+                                        int64_t sa_skb, const uint8_t* qw, int64_t ldw, int64_t w_es,
+                                        const uint8_t* sw, int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+                                        const int32_t* offsets, int64_t E, int64_t total_rows, uint16_t* c,
+                                        int64_t ldc, int64_t N, int64_t K, int in_core, hipStream_t st) {
+  if (in_core)
+    return grouped_dispatch<3>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E,
+                               total_rows, c, ldc, N, K, st);
+  return grouped_dispatch<2>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es, offsets, E,
+                             total_rows, c, ldc, N, K, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -642,6 +814,30 @@ __global__ __launch_bounds__(64) void k_debug_mfma(const uint8_t* __restrict__ a
 
 hipError_t launch_debug_mfma(const uint8_t* a, const uint8_t* b, const float* cin, float* d, hipStream_t st) {
   hipLaunchKernelGGL(k_debug_mfma, dim3(1), dim3(64), 0, st, a, b, cin, d);
+  return hipGetLastError();
+}
+
+// Diagnostic: one v_mfma_scale_f32_16x16x128_f8f6f4 as the E8M0 GEMMs issue
+// it (the lane's row / column byte, the same for its four 32-value blocks).
+__global__ __launch_bounds__(64) void k_debug_mfma_e8m0(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                        const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb,
+                                                        const float* __restrict__ cin, float* __restrict__ d) {
+  const int lane = threadIdx.x, l16 = lane & 15, lgrp = lane >> 4;
+  const uint4 alo = *reinterpret_cast<const uint4*>(a + l16 * 128 + lgrp * 32);
+  const uint4 ahi = *reinterpret_cast<const uint4*>(a + l16 * 128 + lgrp * 32 + 16);
+  const uint4 blo = *reinterpret_cast<const uint4*>(b + l16 * 128 + lgrp * 32);
+  const uint4 bhi = *reinterpret_cast<const uint4*>(b + l16 * 128 + lgrp * 32 + 16);
+  const v8i av = (v8i){(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+  const v8i bv = (v8i){(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+  v4f c;
+  for (int i = 0; i < 4; ++i) c[i] = cin[(lgrp * 4 + i) * 16 + l16];
+  c = mfma_16x16x128_fp8_e8m0(av, bv, c, sa[l16], sb[l16]);
+  for (int i = 0; i < 4; ++i) d[(lgrp * 4 + i) * 16 + l16] = c[i];
+}
+
+hipError_t launch_debug_mfma_e8m0(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                  const float* cin, float* d, hipStream_t st) {
+  hipLaunchKernelGGL(k_debug_mfma_e8m0, dim3(1), dim3(64), 0, st, a, b, sa, sb, cin, d);
   return hipGetLastError();
 }
 

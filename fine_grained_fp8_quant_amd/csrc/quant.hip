@@ -13,6 +13,11 @@
 //   P3 "How I Improved My Deepseek In In The Future" (youlimart.com),
 //      paragraph 3: fusing layer normalisation with the FP8 cast.
 //
+// Each kernel comes in two scale formats: a binary32 scale s = a / 448, and
+// a power-of-two scale stored as an E8M0 byte (the microscaling block-scale
+// format that the pages relate the method to: P1 paragraph 4, P4 paragraph 3;
+// gfx950's matrix core applies such scales itself).
+//
 // All three are HBM-bound streaming kernels: 16-byte coalesced loads, a lane
 // group reduction for the max-abs, one correctly rounded division pair per
 // group, then multiply / clamp / hardware E4M3 convert.  This file is built
@@ -30,9 +35,10 @@ namespace fgq {
 // issues all of its loads before any arithmetic.
 constexpr int kActU = 4;
 
+template <class SF>
 __global__ __launch_bounds__(256) void k_quant_act_1x128(
     const uint16_t* __restrict__ x, int64_t ldx, uint32_t KB, uint32_t n_tiles,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm, int64_t s_skb) {
+    uint8_t* __restrict__ q, int64_t ldq, typename SF::T* __restrict__ s, int64_t s_sm, int64_t s_skb) {
   const uint32_t lane16 = threadIdx.x & 15u;
   const uint32_t grp = threadIdx.x >> 4;
   const uint32_t base = blockIdx.x * (16u * kActU) + grp;
@@ -53,30 +59,43 @@ __global__ __launch_bounds__(256) void k_quant_act_1x128(
     float f[8];
     unpack8(v[u], f);
     const float a = max16(absmax8(f));
-    float sc, r;
-    group_scales(a, sc, r);
+    typename SF::T sc;
+    float r;
+    SF::derive(a, sc, r);
     store_nt8(q + (int64_t)mm[u] * ldq + kk[u] * 128u + lane16 * 8u, cast8(f, r));
     if (lane16 == 0) s[(int64_t)mm[u] * s_sm + (int64_t)kk[u] * s_skb] = sc;
   }
 }
 
-hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
-                                  int64_t ldq, float* s, int64_t s_sm, int64_t s_skb, hipStream_t st) {
+template <class SF>
+static hipError_t launch_act(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q, int64_t ldq,
+                             typename SF::T* s, int64_t s_sm, int64_t s_skb, hipStream_t st) {
   const uint32_t KB = (uint32_t)(K / 128);
   const uint32_t n_tiles = (uint32_t)(M * KB);
   const uint32_t grid = (n_tiles + 16u * kActU - 1) / (16u * kActU);
-  hipLaunchKernelGGL(k_quant_act_1x128, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, q, ldq, s,
+  hipLaunchKernelGGL(k_quant_act_1x128<SF>, dim3(grid), dim3(256), 0, st, x, ldx, KB, n_tiles, q, ldq, s,
                      s_sm, s_skb);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                  int64_t ldq, float* s, int64_t s_sm, int64_t s_skb, hipStream_t st) {
+  return launch_act<ScaleF32>(x, ldx, M, K, q, ldq, s, s_sm, s_skb, st);
+}
+
+hipError_t launch_quant_act_1x128_e8m0(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,
+                                       int64_t ldq, uint8_t* s, int64_t s_sm, int64_t s_skb, hipStream_t st) {
+  return launch_act<ScaleE8M0>(x, ldx, M, K, q, ldq, s, s_sm, s_skb, st);
 }
 
 // ---------------------------------------------------------------------------
 // 128x128 weight blocks.  One workgroup per block: lane t reads 16 bytes of
 // rows (t/16) + 16p, p = 0..7, keeps the 64 values in registers, and the
 // block max-abs goes 16-lane DPP -> wave shuffle -> LDS across the 4 waves.
+template <class SF>
 __global__ __launch_bounds__(256) void k_quant_w_128x128(
     const uint16_t* __restrict__ w, int64_t ldw, int64_t w_bs, uint32_t NB, uint32_t KB,
-    uint8_t* __restrict__ q, int64_t ldq, int64_t q_bs, float* __restrict__ s, int64_t s_snb,
+    uint8_t* __restrict__ q, int64_t ldq, int64_t q_bs, typename SF::T* __restrict__ s, int64_t s_snb,
     int64_t s_skb, int64_t s_bs) {
   __shared__ float red[4];
   uint32_t id = blockIdx.x;
@@ -104,8 +123,9 @@ __global__ __launch_bounds__(256) void k_quant_w_128x128(
   if ((threadIdx.x & 63u) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float sc, r;
-  group_scales(a, sc, r);
+  typename SF::T sc;
+  float r;
+  SF::derive(a, sc, r);
   uint8_t* dst = q + (int64_t)b * q_bs + ((int64_t)nb * 128 + r0) * ldq + kb * 128u + c * 8u;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
@@ -116,14 +136,27 @@ __global__ __launch_bounds__(256) void k_quant_w_128x128(
   if (threadIdx.x == 0) s[(int64_t)b * s_bs + (int64_t)nb * s_snb + (int64_t)kb * s_skb] = sc;
 }
 
+template <class SF>
+static hipError_t launch_w(const uint16_t* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N, int64_t K,
+                           uint8_t* q, int64_t ldq, int64_t q_bs, typename SF::T* s, int64_t s_snb,
+                           int64_t s_skb, int64_t s_bs, hipStream_t st) {
+  const uint32_t NB = (uint32_t)(N / 128), KB = (uint32_t)(K / 128);
+  const uint32_t grid = (uint32_t)(B * NB * KB);
+  hipLaunchKernelGGL(k_quant_w_128x128<SF>, dim3(grid), dim3(256), 0, st, w, ldw, w_bs, NB, KB, q, ldq,
+                     q_bs, s, s_snb, s_skb, s_bs);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N,
                                   int64_t K, uint8_t* q, int64_t ldq, int64_t q_bs, float* s,
                                   int64_t s_snb, int64_t s_skb, int64_t s_bs, hipStream_t st) {
-  const uint32_t NB = (uint32_t)(N / 128), KB = (uint32_t)(K / 128);
-  const uint32_t grid = (uint32_t)(B * NB * KB);
-  hipLaunchKernelGGL(k_quant_w_128x128, dim3(grid), dim3(256), 0, st, w, ldw, w_bs, NB, KB, q, ldq,
-                     q_bs, s, s_snb, s_skb, s_bs);
-  return hipGetLastError();
+  return launch_w<ScaleF32>(w, ldw, w_bs, B, N, K, q, ldq, q_bs, s, s_snb, s_skb, s_bs, st);
+}
+
+hipError_t launch_quant_w_128x128_e8m0(const uint16_t* w, int64_t ldw, int64_t w_bs, int64_t B, int64_t N,
+                                       int64_t K, uint8_t* q, int64_t ldq, int64_t q_bs, uint8_t* s,
+                                       int64_t s_snb, int64_t s_skb, int64_t s_bs, hipStream_t st) {
+  return launch_w<ScaleE8M0>(w, ldw, w_bs, B, N, K, q, ldq, q_bs, s, s_snb, s_skb, s_bs, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -139,11 +172,11 @@ hipError_t launch_quant_w_128x128(const uint16_t* w, int64_t ldw, int64_t w_bs, 
 // t does the two correctly rounded divisions of tile t (once per tile rather
 // than once per lane of each 16-lane group).  gamma is widened into LDS once
 // per workgroup; FULL drops the bounds guards when K = 512 NI.
-template <int NI, bool FULL>
+template <class SF, int NI, bool FULL>
 __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
-    uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm,
-    int64_t s_skb) {
+    uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, typename SF::T* __restrict__ s,
+    int64_t s_sm, int64_t s_skb) {
   static_assert(NI <= 16, "one tile per lane in the scale pass");
   __shared__ float tile_slot[4][64];
   // gamma widened once per workgroup (not once per row): plane 0 holds
@@ -203,8 +236,9 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (lane < ntiles) {
-      float sc, r;
-      group_scales(slot[lane], sc, r);
+      typename SF::T sc;
+      float r;
+      SF::derive(slot[lane], sc, r);
       s[(int64_t)row * s_sm + (int64_t)lane * s_skb] = sc;
       slot[lane] = r;
     }
@@ -220,11 +254,11 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_regs(
 
 // Long rows (K up to 16384): the row stays packed BF16 in registers and is
 // widened again for each pass; scales are computed per 16-lane group.
-template <int NI>
+template <class SF, int NI>
 __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_long(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
-    uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t s_sm,
-    int64_t s_skb) {
+    uint32_t M, uint32_t K, uint8_t* __restrict__ q, int64_t ldq, typename SF::T* __restrict__ s,
+    int64_t s_sm, int64_t s_skb) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
   if (row >= M) return;  // whole wave leaves together
@@ -264,41 +298,55 @@ __global__ __launch_bounds__(256) void k_fused_rmsnorm_quant_long(
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = (f[j] * rstd) * g[j];
       const float a = max16(absmax8(y));
-      float sc, r;
-      group_scales(a, sc, r);
+      typename SF::T sc;
+      float r;
+      SF::derive(a, sc, r);
       store_nt8(qr + vi * 8u, cast8(y, r));
       if ((lane & 15u) == 0) s[(int64_t)row * s_sm + (int64_t)(vi >> 4) * s_skb] = sc;
     }
   }
 }
 
-template <int NI>
+template <class SF, int NI>
 static void launch_fused_regs(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t M,
-                              int64_t K, uint8_t* q, int64_t ldq, float* s, int64_t s_sm, int64_t s_skb,
-                              hipStream_t st) {
+                              int64_t K, uint8_t* q, int64_t ldq, typename SF::T* s, int64_t s_sm,
+                              int64_t s_skb, hipStream_t st) {
   const dim3 grid((uint32_t)((M + 3) / 4));
   if (K == 512 * NI)  // rows that fill the registers exactly: no per-vector guards
-    hipLaunchKernelGGL((k_fused_rmsnorm_quant_regs<NI, true>), grid, dim3(256), 0, st, x, ldx,
+    hipLaunchKernelGGL((k_fused_rmsnorm_quant_regs<SF, NI, true>), grid, dim3(256), 0, st, x, ldx,
                        gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
   else
-    hipLaunchKernelGGL((k_fused_rmsnorm_quant_regs<NI, false>), grid, dim3(256), 0, st, x, ldx,
+    hipLaunchKernelGGL((k_fused_rmsnorm_quant_regs<SF, NI, false>), grid, dim3(256), 0, st, x, ldx,
                        gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+}
+
+template <class SF>
+static hipError_t launch_fused(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t M,
+                               int64_t K, uint8_t* q, int64_t ldq, typename SF::T* s, int64_t s_sm,
+                               int64_t s_skb, hipStream_t st) {
+  const int64_t ni = (K / 8 + 63) / 64;
+  if (ni <= 2) launch_fused_regs<SF, 2>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 4) launch_fused_regs<SF, 4>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 8) launch_fused_regs<SF, 8>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 12) launch_fused_regs<SF, 12>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 14) launch_fused_regs<SF, 14>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else if (ni <= 16) launch_fused_regs<SF, 16>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+  else
+    hipLaunchKernelGGL((k_fused_rmsnorm_quant_long<SF, 32>), dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, st, x,
+                       ldx, gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
                                       int64_t M, int64_t K, uint8_t* q, int64_t ldq, float* s,
                                       int64_t s_sm, int64_t s_skb, hipStream_t st) {
-  const int64_t ni = (K / 8 + 63) / 64;
-  if (ni <= 2) launch_fused_regs<2>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
-  else if (ni <= 4) launch_fused_regs<4>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
-  else if (ni <= 8) launch_fused_regs<8>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
-  else if (ni <= 12) launch_fused_regs<12>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
-  else if (ni <= 14) launch_fused_regs<14>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
-  else if (ni <= 16) launch_fused_regs<16>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
-  else
-    hipLaunchKernelGGL(k_fused_rmsnorm_quant_long<32>, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, st, x, ldx,
-                       gamma, eps, (uint32_t)M, (uint32_t)K, q, ldq, s, s_sm, s_skb);
-  return hipGetLastError();
+  return launch_fused<ScaleF32>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
+}
+
+hipError_t launch_fused_rmsnorm_quant_e8m0(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                                           int64_t M, int64_t K, uint8_t* q, int64_t ldq, uint8_t* s,
+                                           int64_t s_sm, int64_t s_skb, hipStream_t st) {
+  return launch_fused<ScaleE8M0>(x, ldx, gamma, eps, M, K, q, ldq, s, s_sm, s_skb, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,11 +1,12 @@
 """Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
 
-    python -m fine_grained_fp8_quant_amd.profile_summary <out_dir> <workload> [...]
+    python -m fine_grained_fp8_quant_amd.profile_summary <out_dir> <workload>[:e8m0] [...]
 
 <out_dir> holds, per workload, the output of the two commands printed in
 each summary (a kernel trace of bench.py, and FETCH_SIZE / WRITE_SIZE
 counter passes of profile_workload.py).  Writes profiles/<workload>_kernels.md
-and updates profiles/traffic.json with HBM bytes per launch.
+(<workload>_e8m0_kernels.md for the power-of-two scale variant) and updates
+profiles/traffic.json with HBM bytes per launch.
 
 Traffic calibration: the counter passes also run a 1 GiB device copy
 (fgq_debug_copy).  Its FETCH_SIZE and WRITE_SIZE against the known 1 GiB
@@ -26,10 +27,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 SOURCES = {"gemm": "fine_grained_fp8_quant_amd/csrc/gemm.hip", "quant": "fine_grained_fp8_quant_amd/csrc/quant.hip",
            "dispatch": "fine_grained_fp8_quant_amd/csrc/dispatch.hip"}
 
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace/{w} -o trace -- "
-             "python -u bench.py --workload {w} --steps 5 --warmup 2 --no-cpu-baseline")
-PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{w}/{c} -o pmc -- "
-           "python -u -m fine_grained_fp8_quant_amd.profile_workload --workload {w}")
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace/{tag} -o trace -- "
+             "python -u bench.py --workload {w} --scales {sc} --steps 5 --warmup 2 --no-cpu-baseline")
+PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{tag}/{c} -o pmc -- "
+           "python -u -m fine_grained_fp8_quant_amd.profile_workload --workload {w} --scales {sc}")
+MODE_NAMES = {"0": "exact", "1": "fp8core", "2": "promote", "3": "incore"}
 
 
 def sha(rel):
@@ -42,26 +44,28 @@ def short(name: str) -> str:
     base = name.split("(")[0].replace("void ", "").replace("fgq::", "")
     m = re.match(r"(k_\w+)<TileCfg<(\d+), (\d+), (\d+), (\d+)(?:, (\d+))?>, (\d)>", base)
     if m:
-        mode = "exact" if m.group(7) == "0" else "fp8core"
-        return f"{m.group(1)}[{m.group(2)}x{m.group(3)},{mode}]"
+        return f"{m.group(1)}[{m.group(2)}x{m.group(3)},{MODE_NAMES[m.group(7)]}]"
     return base
 
 
-def api_of(kname: str):
-    """(C-ABI call name, mode) a kernel belongs to."""
+def api_of(kname: str, e8: bool):
+    """(C-ABI call name, mode) a kernel belongs to; ``e8`` says the run used
+    power-of-two scales (the routing kernels and the split-K reduction carry
+    no scale type of their own)."""
+    sfx = "_e8m0" if e8 else ""
     if kname.startswith("k_quant_act"):
-        return "quant_act_1x128", None
+        return "quant_act_1x128" + sfx, None
     if kname.startswith("k_quant_w"):
-        return "quant_w_128x128", None
+        return "quant_w_128x128" + sfx, None
     if kname.startswith("k_fused"):
-        return "fused_rmsnorm_quant", None
+        return "fused_rmsnorm_quant" + sfx, None
     if kname.startswith("k_dispatch"):
-        return "quant_dispatch_1x128", None
-    mode = "exact" if "exact" in kname else ("fp8core" if "fp8core" in kname else None)
+        return "quant_dispatch_1x128" + sfx, None
+    mode = next((m for m in MODE_NAMES.values() if "," + m + "]" in kname), None)
     if kname.startswith("k_grouped"):
-        return "grouped_gemm_fp8_blockscaled", mode
+        return ("grouped_gemm_fp8_e8m0" if e8 else "grouped_gemm_fp8_blockscaled"), mode
     if kname.startswith("k_gemm") or kname.startswith("k_splitk"):
-        return "gemm_fp8_blockscaled", mode
+        return ("gemm_fp8_e8m0" if e8 else "gemm_fp8_blockscaled"), mode
     return None, None
 
 
@@ -84,10 +88,14 @@ def read_pmc(path):
     return [(k, v) for _, k, v in out]
 
 
-def summarise(out_dir, w, traffic):
-    stats = read_stats(os.path.join(out_dir, "trace", w, "trace_kernel_stats.csv"))
-    fetch = read_pmc(os.path.join(out_dir, "pmc", w, "FETCH_SIZE", "pmc_counter_collection.csv"))
-    write = read_pmc(os.path.join(out_dir, "pmc", w, "WRITE_SIZE", "pmc_counter_collection.csv"))
+def summarise(out_dir, spec, traffic):
+    w, _, sc = spec.partition(":")
+    sc = sc or "f32"
+    e8 = sc == "e8m0"
+    tag = w + ("_e8m0" if e8 else "")
+    stats = read_stats(os.path.join(out_dir, "trace", tag, "trace_kernel_stats.csv"))
+    fetch = read_pmc(os.path.join(out_dir, "pmc", tag, "FETCH_SIZE", "pmc_counter_collection.csv"))
+    write = read_pmc(os.path.join(out_dir, "pmc", tag, "WRITE_SIZE", "pmc_counter_collection.csv"))
     gib_kib = 1024 * 1024
     f_copy = [v for k, v in fetch if k.startswith("k_debug_copy")][0]
     w_copy = [v for k, v in write if k.startswith("k_debug_copy")][0]
@@ -97,11 +105,12 @@ def summarise(out_dir, w, traffic):
         per_kernel[k][0].append(v * f_factor * 1024)
     for k, v in write:
         per_kernel[k][1].append(v * w_factor * 1024)
-    lines = [f"# {w}: kernel durations and HBM traffic (one MI355X)", "",
+    title = w + (" with power-of-two (E8M0) scales" if e8 else "")
+    lines = [f"# {title}: kernel durations and HBM traffic (one MI355X)", "",
              "Commands (from the repository root; `<out>` is any scratch directory):", "",
-             "    " + TRACE_CMD.format(w=w), "    " + PMC_CMD.format(w=w, c="FETCH_SIZE"),
-             "    " + PMC_CMD.format(w=w, c="WRITE_SIZE"),
-             "    python -m fine_grained_fp8_quant_amd.profile_summary <out> " + w, "",
+             "    " + TRACE_CMD.format(w=w, sc=sc, tag=tag), "    " + PMC_CMD.format(w=w, sc=sc, tag=tag, c="FETCH_SIZE"),
+             "    " + PMC_CMD.format(w=w, sc=sc, tag=tag, c="WRITE_SIZE"),
+             "    python -m fine_grained_fp8_quant_amd.profile_summary <out> " + spec, "",
              "## Kernel trace (`--kernel-trace --stats`; includes warm-up calls)", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
@@ -117,10 +126,10 @@ def summarise(out_dir, w, traffic):
         rd = sum(fs) / len(fs)
         wr = sum(ws) / len(ws) if ws else 0.0
         lines.append(f"| {k} | {len(fs)} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
-        api, mode = api_of(k)
+        api, mode = api_of(k, e8)
         if api:
             # the split-K reduction runs once per dense GEMM call in either mode
-            modes = [mode] if mode or "gemm" not in api else ["exact", "fp8core"]
+            modes = [mode] if mode or "gemm" not in api else (["promote", "incore"] if e8 else ["exact", "fp8core"])
             for md in modes:
                 key = f"{w}/{api}" + (f"[{md}]" if md else "")
                 sums[key][0] += rd
@@ -129,7 +138,7 @@ def summarise(out_dir, w, traffic):
     for key, (rd, wr, src) in sums.items():
         traffic[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr, "source_sha": src}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, f"{w}_kernels.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"{tag}_kernels.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 

@@ -57,7 +57,7 @@ enum {
   FGQ_ERR_HIP = 6          /* a HIP launch failed; see fgq_last_hip_error() */
 };
 
-#define FGQ_ABI_VERSION 2
+#define FGQ_ABI_VERSION 3
 
 /*
  * fgq_quant_act_1x128 -- online activation quantisation, one scale per
@@ -249,6 +249,101 @@ fgq_status_t fgq_quant_dispatch_1x128(const void* x, int64_t ldx, int64_t T, int
 /* Bytes of workspace fgq_quant_dispatch_1x128 needs (0 = none). */
 size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E);
 
+/*
+ * Power-of-two (E8M0) scales.  The pages note that per-group scaling along K
+ * is in line with microscaling formats, and that newer matrix units support
+ * such formats natively [P1 paragraph 4, P4 paragraph 3].  A microscaling
+ * block scale is an E8M0 byte (OCP Microscaling Formats v1.0): the value
+ * 2^(byte - 127); byte 255 is NaN.  gfx950's FP8 matrix core multiplies such
+ * scales in itself (v_mfma_scale_f32_16x16x128_f8f6f4), so the GEMMs below
+ * need no binary32 scale products.
+ *
+ * Scale rule (in place of s = a / 448): for a group with max-abs a, the
+ * smallest e >= -127 with 448 * 2^e >= a; the stored byte is e + 127 (a = 0
+ * gives byte 0).  The cast multiplies by 2^-e, which is exact, so
+ *     q_j = E4M3_rne(x_j * 2^-e),   |x_j * 2^-e| <= 448,
+ *     value ~= decode(q_j) * 2^(byte - 127).
+ * Scale arrays are bytes with strides in bytes and no alignment rule.  The
+ * GEMMs read each scale as the aligned 32-bit word that holds it (that word
+ * must be readable memory, as it is inside any allocation).
+ */
+
+/* fgq_quant_act_1x128_e8m0 -- fgq_quant_act_1x128 with E8M0 scales:
+ * s[m * s_sm + kb * s_skb] = byte of tile (m, kb).  Bit-identical to the rule above. */
+fgq_status_t fgq_quant_act_1x128_e8m0(const void* x, int64_t ldx, int64_t M, int64_t K,
+                                      void* q, int64_t ldq, uint8_t* s, int64_t s_sm, int64_t s_skb,
+                                      void* stream);
+
+/* fgq_quant_w_128x128_e8m0 -- fgq_quant_w_128x128 with E8M0 scales:
+ * s[b * s_bs + nb * s_snb + kb * s_skb] = byte of block (b, nb, kb). */
+fgq_status_t fgq_quant_w_128x128_e8m0(const void* w, int64_t ldw, int64_t w_bs, int64_t B,
+                                      int64_t N, int64_t K, void* q, int64_t ldq, int64_t q_bs,
+                                      uint8_t* s, int64_t s_snb, int64_t s_skb, int64_t s_bs,
+                                      void* stream);
+
+/* fgq_fused_rmsnorm_quant_e8m0 -- fgq_fused_rmsnorm_quant (same y) with E8M0
+ * scales of the binary32 tile max-abs of y. */
+fgq_status_t fgq_fused_rmsnorm_quant_e8m0(const void* x, int64_t ldx, const void* gamma, float eps,
+                                          int64_t M, int64_t K, void* q, int64_t ldq,
+                                          uint8_t* s, int64_t s_sm, int64_t s_skb, void* stream);
+
+/* fgq_quant_dispatch_1x128_e8m0 -- fgq_quant_dispatch_1x128 with E8M0 scales
+ * (s[r * s_sm + kb * s_skb], bytes): every routed row is bit-identical to
+ * fgq_quant_act_1x128_e8m0 of its token row.  Same routing outputs. */
+fgq_status_t fgq_quant_dispatch_1x128_e8m0(const void* x, int64_t ldx, int64_t T, int64_t K,
+                                           const int32_t* ids, int64_t topk, int64_t E, void* q,
+                                           int64_t ldq, uint8_t* s, int64_t s_sm, int64_t s_skb,
+                                           int32_t* offsets, int32_t* row_src, int32_t* dest,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * How the E8M0 GEMMs accumulate across 128-wide K chunks.  Each chunk is one
+ * scaled matrix-core operation per 16x16 output block; scales are applied by
+ * the unit.
+ *
+ * FGQ_E8M0_PROMOTE (default): each chunk's scaled sum lands in a fresh zero
+ *   accumulator and is added to a binary32 accumulator on the vector ALU:
+ *   the pages' promotion at an interval of 128 [P1 paragraph 4,
+ *   P4 paragraph 4].  Same accuracy as FGQ_GEMM_FP8_CORE.
+ * FGQ_E8M0_IN_CORE: the running sum is the matrix core's own accumulator
+ *   operand, so no vector-ALU work at all: the accumulation without
+ *   promotion that the pages warn about on H800, where about 14 bits survive.
+ *   Measured on gfx950: the unit aligns the accumulator operand and the
+ *   chunk's 8-product group sums to the largest of them and truncates what
+ *   falls more than about 24 bits below, so each chunk costs at most about
+ *   2^-20 of the running sum (the 13-bit window inside each group is the
+ *   same in both modes).  Accuracy is that of FGQ_E8M0_PROMOTE to within
+ *   BF16 output rounding.
+ */
+enum { FGQ_E8M0_PROMOTE = 0, FGQ_E8M0_IN_CORE = 1 };
+
+/*
+ * fgq_gemm_fp8_e8m0 -- fgq_gemm_fp8_blockscaled with E8M0 scales:
+ *     C[m, n] = bf16( sum_kb 2^(sa[m, kb] - 127) * 2^(sw[n/128, kb] - 127)
+ *                            * sum_{k in chunk kb} decode(qa[m, k]) * decode(qw[n, k]) )
+ *   sa     bytes, sa[m * sa_sm + kb * sa_skb].
+ *   sw     bytes, sw[nb * sw_snb + kb * sw_skb].
+ *   accumulate  FGQ_E8M0_PROMOTE or FGQ_E8M0_IN_CORE (else FGQ_ERR_UNSUPPORTED).
+ *   Everything else (shapes, strides, alignment, workspace =
+ *   fgq_gemm_workspace_bytes(M, N, K)) as in fgq_gemm_fp8_blockscaled.
+ */
+fgq_status_t fgq_gemm_fp8_e8m0(const void* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm,
+                               int64_t sa_skb, const void* qw, int64_t ldw, const uint8_t* sw,
+                               int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K, int32_t accumulate, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* fgq_grouped_gemm_fp8_e8m0 -- fgq_grouped_gemm_fp8_blockscaled with E8M0
+ * scales (sw[e * sw_es + nb * sw_snb + kb * sw_skb], bytes) and the
+ * accumulation choice of fgq_gemm_fp8_e8m0. */
+fgq_status_t fgq_grouped_gemm_fp8_e8m0(const void* qa, int64_t lda, const uint8_t* sa,
+                                       int64_t sa_sm, int64_t sa_skb, const void* qw,
+                                       int64_t ldw, int64_t w_es, const uint8_t* sw,
+                                       int64_t sw_snb, int64_t sw_skb, int64_t sw_es,
+                                       const int32_t* offsets, int64_t E, int64_t total_rows,
+                                       void* c, int64_t ldc, int64_t N, int64_t K, int32_t accumulate,
+                                       void* stream);
+
 /* Text for a status code (static storage; never NULL). */
 const char* fgq_status_string(fgq_status_t status);
 
@@ -276,6 +371,13 @@ fgq_status_t fgq_debug_copy(const void* src, void* dst, int64_t bytes, void* str
  * aligned), cin and d float [16][16] row-major.  Used to measure how the unit
  * accumulates a 128-wide chunk (the pages report ~14 retained bits on H800). */
 fgq_status_t fgq_debug_mfma_16x16x128(const void* a, const void* b, const float* cin, float* d, void* stream);
+
+/* fgq_debug_mfma_e8m0_16x16x128 -- one scaled FP8 matrix-core operation as
+ * the E8M0 GEMMs issue it: d = diag(2^(sa - 127)) a b^T diag(2^(sb - 127)) + cin,
+ * sa and sb bytes [16] (row scales of a, column scales of b), the rest as in
+ * fgq_debug_mfma_16x16x128.  Used to measure how the unit adds cin. */
+fgq_status_t fgq_debug_mfma_e8m0_16x16x128(const void* a, const void* b, const uint8_t* sa,
+                                           const uint8_t* sb, const float* cin, float* d, void* stream);
 
 #ifdef __cplusplus
 }

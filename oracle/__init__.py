@@ -64,6 +64,7 @@ from .gemm import (  # noqa: F401
 )
 from .dispatch import (  # noqa: F401
     dispatch_ref,
+    quant_dispatch_e8m0_ref,
     quant_dispatch_ref,
 )
 from .e8m0 import (  # noqa: F401

@@ -53,3 +53,15 @@ def quant_dispatch_ref(x_bits: np.ndarray, ids: np.ndarray, n_experts: int):
     tokens = row_src.astype(np.int64) // topk
     q, s = quant_act_1x128(np.asarray(x_bits)[tokens])
     return q, s, offsets, row_src, dest
+
+
+def quant_dispatch_e8m0_ref(x_bits: np.ndarray, ids: np.ndarray, n_experts: int):
+    """As ``quant_dispatch_ref`` with power-of-two scales (``oracle.e8m0``):
+    ``(q [R, K], E8M0 bytes [R, K/128], offsets, row_src, dest)``."""
+    from .e8m0 import quant_act_1x128_e8m0
+    ids = np.asarray(ids)
+    topk = ids.shape[1] if ids.ndim == 2 else 1
+    offsets, row_src, dest = dispatch_ref(ids, n_experts)
+    tokens = row_src.astype(np.int64) // topk
+    q, b = quant_act_1x128_e8m0(np.asarray(x_bits)[tokens])
+    return q, b, offsets, row_src, dest

@@ -32,7 +32,9 @@ def declared_functions():
 def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("fgq_quant_act_1x128", "fgq_quant_w_128x128", "fgq_fused_rmsnorm_quant",
-              "fgq_gemm_fp8_blockscaled", "fgq_grouped_gemm_fp8_blockscaled", "fgq_quant_dispatch_1x128"):
+              "fgq_gemm_fp8_blockscaled", "fgq_grouped_gemm_fp8_blockscaled", "fgq_quant_dispatch_1x128",
+              "fgq_quant_act_1x128_e8m0", "fgq_quant_w_128x128_e8m0", "fgq_fused_rmsnorm_quant_e8m0",
+              "fgq_gemm_fp8_e8m0", "fgq_grouped_gemm_fp8_e8m0", "fgq_quant_dispatch_1x128_e8m0"):
         assert n in names
 
 
@@ -42,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fgq_abi_version() == 2
+    assert lib.fgq_abi_version() == 3
     for code in range(7):
         assert lib.fgq_status_string(code)
     assert lib.fgq_status_string(99) == b"unknown status"
@@ -204,3 +206,68 @@ def test_dispatch_validation(lib):
     assert lib.fgq_quant_dispatch_workspace_bytes(0, 8, 32) == 0
     assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32) == 2 * (4096 * 8 // 256) * 32 * 4   # 256-pair blocks
     assert lib.fgq_quant_dispatch_workspace_bytes(-1, 8, 32) == 0
+
+
+# ---- power-of-two (E8M0) scale variants: byte scales, no alignment rule on them
+
+def test_quant_e8m0_validation(lib):
+    a8 = lib.fgq_quant_act_1x128_e8m0
+    assert a8(P, 256, -1, 256, Q, 256, S, 2, 1, None) == SHAPE
+    assert a8(P, 256, 4, 100, Q, 256, S, 2, 1, None) == UNSUP
+    assert a8(P, 256, 0, 256, Q, 256, S, 2, 1, None) == OK
+    assert a8(P, 256, 4, 256, Q, 256, 0, 2, 1, None) == NULL
+    assert a8(P, 256, 4, 256, Q + 8, 256, S + 1, 2, 1, None) == ALIGN    # the codes, not the bytes
+    assert a8(P, 256, 4, 256, Q, 256, S + 1, -1, 1, None) == STRIDE     # byte scales pass the alignment check
+    assert act(lib, s=S + 1, s_sm=-1) == ALIGN                           # binary32 scales do not
+    w8 = lib.fgq_quant_w_128x128_e8m0
+    assert w8(P, 256, 256 * 128, 2, 100, 256, Q, 256, 256 * 128, S, 2, 1, 2, None) == UNSUP
+    assert w8(P, 256, 256 * 128, 0, 128, 256, Q, 256, 256 * 128, S, 2, 1, 2, None) == OK
+    assert w8(P, 256, 256 * 128, 2, 128, 256, Q, 256, 256 * 128, S + 3, -2, 1, 2, None) == STRIDE
+    f8 = lib.fgq_fused_rmsnorm_quant_e8m0
+    assert f8(P, 256, 0, ctypes.c_float(1e-6), 4, 256, Q, 256, S, 2, 1, None) == NULL
+    assert f8(P, 32768, Q, ctypes.c_float(1e-6), 4, 32768, Q, 32768, S + 1, 256, 1, None) == UNSUP
+
+
+def gemm8(lib, qa=P, lda=256, sa=S, sa_sm=2, sa_skb=1, qw=Q, ldw=256, sw=S, sw_snb=2, sw_skb=1, c=Q,
+          ldc=256, M=4, N=256, K=256, acc=0, ws=0, ws_bytes=0):
+    return lib.fgq_gemm_fp8_e8m0(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc,
+                                 M, N, K, acc, ws, ws_bytes, None)
+
+
+def test_gemm_e8m0_validation(lib):
+    assert gemm8(lib, M=-1) == SHAPE
+    assert gemm8(lib, acc=2) == UNSUP
+    assert gemm8(lib, acc=-1) == UNSUP
+    assert gemm8(lib, K=200) == UNSUP
+    assert gemm8(lib, M=0) == OK
+    assert gemm8(lib, sa=0) == NULL
+    assert gemm8(lib, sw=0) == NULL
+    assert gemm8(lib, c=Q + 2) == ALIGN
+    assert gemm8(lib, sa=S + 1, sw=S + 3, lda=128) == STRIDE       # unaligned byte scales are fine
+    assert gemm(lib, sa=S + 1, lda=128) == ALIGN                    # unaligned binary32 scales are not
+    need = lib.fgq_gemm_workspace_bytes(64, 18432, 7168)
+    assert gemm8(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL      # no workspace
+    assert gemm8(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
+    g8 = lib.fgq_grouped_gemm_fp8_e8m0
+    assert g8(P, 256, S, 2, 1, Q, 256, 256 * 256, S, 2, 1, 4, S, 4, 100, Q, 256, 256, 256, 5, None) == UNSUP
+    assert g8(P, 256, S, 2, 1, Q, 256, 256 * 256, S, 2, 1, 4, S, 0, 100, Q, 256, 256, 256, 1, None) == OK
+    assert g8(P, 256, S, 2, 1, Q, 256, 256 * 256, S, 2, 1, 4, 0, 4, 100, Q, 256, 256, 256, 1, None) == NULL
+    assert g8(P, 256, S + 1, 2, 1, Q, 256, 100 * 16, S + 1, 2, 1, 4, S, 4, 100, Q, 256, 256, 256, 0, None) == STRIDE
+    assert lib.fgq_debug_mfma_e8m0_16x16x128(P, Q, 0, S, S, S, None) == NULL
+    assert lib.fgq_debug_mfma_e8m0_16x16x128(P + 8, Q, S, S, S, S, None) == ALIGN
+
+
+def test_dispatch_e8m0_validation(lib):
+    d8 = lib.fgq_quant_dispatch_1x128_e8m0
+    args = dict(x=P, ldx=256, T=4, K=256, ids=S, topk=2, E=3, q=Q, ldq=256, s=S + 1025, s_sm=1, s_skb=8,
+                off=S + 2048, src=S + 3072, dest=S + 4096, ws=P + 65536, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return d8(a["x"], a["ldx"], a["T"], a["K"], a["ids"], a["topk"], a["E"], a["q"], a["ldq"], a["s"], a["s_sm"],
+                  a["s_skb"], a["off"], a["src"], a["dest"], a["ws"], a["ws_bytes"], None)
+    assert call(T=-1) == SHAPE
+    assert call(E=4097) == UNSUP
+    assert call(off=0) == NULL
+    assert call(ldq=128) == STRIDE          # an odd scale address passes the alignment check
+    assert dispatch(lib, s=S + 1025, ldq=128) == ALIGN
