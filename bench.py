@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--scales", default="f32", choices=["f32", "e8m0"],
                    help="scale format: binary32 (a/448) or power-of-two E8M0 bytes")
+    p.add_argument("--fused-a", action="store_true",
+                   help="prefill/decode: quantise A inside the GEMM's A-load (gemm_bf16a_fp8_blockscaled) "
+                        "instead of a separate quant_act_1x128 launch")
     p.add_argument("--mode", default=None, choices=["exact", "fp8core", "promote", "incore"],
                    help="GEMM accumulation. f32 scales: exact products (FP16 matrix cores, default) or FP8 "
                         "matrix cores; e8m0 scales: promote (default) or incore")
@@ -77,6 +80,8 @@ def parse():
         args.mode = modes[0]
     if args.mode not in modes:
         p.error(f"--mode {args.mode} does not apply to --scales {args.scales} (use {' or '.join(modes)})")
+    if args.fused_a and (args.scales != "f32" or args.workload not in ("prefill", "decode")):
+        p.error("--fused-a applies to the prefill and decode workloads with binary32 scales")
     return args
 
 
@@ -262,6 +267,12 @@ def make_step(args, fgq, d, n_sets, mode):
             return
         if args.workload == "fused_down":
             t.run(nm["fused_rmsnorm_quant"], lambda: api.fused(s["X"], s["G"], eps, q=o["qx"], s=o["sx"]))
+        if args.fused_a:
+            t.run(nm["quant_w_128x128"], lambda: api.quant_w(s["W"], q=o["qw"], s=o["sw"]))
+            t.run("gemm_bf16a_fp8_blockscaled",
+                  lambda: fgq.gemm_bf16a_fp8_blockscaled(s["A"], o["qw"], o["sw"], out=o["c"], workspace=o["ws"],
+                                                         mode=mode))
+            return
         t.run(nm["quant_act_1x128"], lambda: api.quant_act(s["A"], q=o["qa"], s=o["sa"]))
         t.run(nm["quant_w_128x128"], lambda: api.quant_w(s["W"], q=o["qw"], s=o["sw"]))
         if args.workload in ("prefill", "decode"):
@@ -455,7 +466,7 @@ def main():
                     "incore": "e8m0 scales applied by the unit, accumulate in the matrix core"}[args.mode],
         "data": "synthetic (seeded, shapes and distributions of the named workload)",
         "config": {"workload": WORKLOAD_TITLES[args.workload], **{k: v for k, v in shape.items() if k != "counts"},
-                   "scales": args.scales, "input_sets": len(sets)},
+                   "scales": args.scales, "fused_a": bool(args.fused_a), "input_sets": len(sets)},
         "roofline": roofline,
         "kernels": kernels,
         "gemm_mode": args.mode,

@@ -12,6 +12,7 @@ Functions (same names as the C ABI in include/fgq.h, without the prefix):
     fused_rmsnorm_quant(x, gamma, eps)     -> (q, s) as quant_act_1x128
     gemm_fp8_blockscaled(qa, sa, qw, sw)   -> c bfloat16 [M, N]
     grouped_gemm_fp8_blockscaled(qa, sa, qw, sw, offsets) -> c bfloat16 [R, N]
+    gemm_bf16a_fp8_blockscaled(a, qw, sw)  -> c: the activation quantisation fused into the GEMM's A-load
     quant_dispatch_1x128(x, ids, E)        -> (q, s, offsets, row_src, dest): FP8 rows grouped by expert
 
 Power-of-two (E8M0) scale variants, scales as uint8 exponent bytes
@@ -42,7 +43,7 @@ __all__ = [
     "debug_encode_e4m3", "debug_copy", "debug_mfma_16x16x128", "STATUS", "GEMM_EXACT", "GEMM_FP8_CORE",
     "quant_act_1x128_e8m0", "quant_w_128x128_e8m0", "fused_rmsnorm_quant_e8m0", "act_scales_e8m0",
     "gemm_fp8_e8m0", "grouped_gemm_fp8_e8m0", "debug_mfma_e8m0_16x16x128", "E8M0_PROMOTE", "E8M0_IN_CORE",
-    "quant_dispatch_1x128_e8m0",
+    "quant_dispatch_1x128_e8m0", "gemm_bf16a_fp8_blockscaled",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -102,6 +103,8 @@ _SIGNATURES = {
     "fgq_grouped_gemm_fp8_e8m0": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                   _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _st, _vp],
     "fgq_debug_mfma_e8m0_16x16x128": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "fgq_gemm_bf16a_fp8_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _st,
+                                       _vp, _i64, _vp, _i64, _i64, _vp, ctypes.c_size_t, _vp],
     "fgq_quant_dispatch_1x128_e8m0": [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                       _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
 }
@@ -384,6 +387,39 @@ def _gemm(fn, sdtype, qa, sa, qw, sw, out, workspace, mode, stream):
     _check(fn(_ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(0), _ptr(sw),
               sw.stride(0), sw.stride(1), _ptr(out), out.stride(0), M, N, K, int(mode), _ptr(workspace), ws_bytes,
               _stream(stream)))
+    return out
+
+
+def gemm_bf16a_fp8_blockscaled(a, qw, sw, out=None, workspace=None, mode=GEMM_EXACT, qa_out=None, sa_out=None,
+                               stream=None):
+    """GEMM of BF16 ``a [M, K]`` with quantised weights, the 1x128 quantisation of
+    ``a`` done inside the GEMM's A-load.  Optional ``qa_out`` (uint8 [M, K]) and
+    ``sa_out`` (float32 [M, K/128] view) receive the codes and scales."""
+    torch = _torch()
+    load_library()
+    qw = _codes(qw)
+    _need(a, torch.bfloat16, "a")
+    _need(qw, torch.uint8, "qw")
+    _need_scales(sw, "sw")
+    M, K = a.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("a and qw disagree on K")
+    if (qa_out is None) != (sa_out is None):
+        raise ValueError("give both qa_out and sa_out, or neither")
+    if sa_out is not None:
+        _need_scales(sa_out, "sa_out")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    need = gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.fgq_gemm_bf16a_fp8_blockscaled(
+        _ptr(a), a.stride(0), _ptr(qw), qw.stride(0), _ptr(sw), sw.stride(0), sw.stride(1), _ptr(out), out.stride(0),
+        M, N, K, int(mode), _ptr(qa_out), qa_out.stride(0) if qa_out is not None else 0, _ptr(sa_out),
+        sa_out.stride(0) if sa_out is not None else 0, sa_out.stride(1) if sa_out is not None else 0,
+        _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

@@ -32,7 +32,9 @@ SOURCES = {
     "dispatch.hip": ["-ffp-contract=off"],
     # MFMA results straight into VGPRs: the per-chunk promotion FMA reads them
     # on the vector ALU, which cannot read AGPRs without an extra move.
-    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # -ffp-contract=off as well: the fused A-load quantisation must match
+    # quant.hip bit for bit.
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-ffp-contract=off"],
     "fgq_api.cpp": [],
 }
 

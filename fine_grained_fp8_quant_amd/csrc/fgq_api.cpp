@@ -190,6 +190,37 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
       as_stream(stream)));
 }
 
+fgq_status_t fgq_gemm_bf16a_fp8_blockscaled(const void* a, int64_t lda, const void* qw, int64_t ldw, const float* sw,
+                                            int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc, int64_t M, int64_t N,
+                                            int64_t K, int32_t mode, void* qa_out, int64_t ldq, float* sa_out,
+                                            int64_t sa_sm, int64_t sa_skb, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FGQ_ERR_SHAPE;
+  if (mode != FGQ_GEMM_EXACT && mode != FGQ_GEMM_FP8_CORE) return FGQ_ERR_UNSUPPORTED;
+  if (N % 128 != 0 || K % 128 != 0 || K == 0) return FGQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FGQ_OK;
+  if (!a || !qw || !sw || !c) return FGQ_ERR_NULL;
+  if ((qa_out == nullptr) != (sa_out == nullptr)) return FGQ_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(qw, 16) || !aligned(c, 16) || !aligned(sw, 4)) return FGQ_ERR_ALIGN;
+  if (lda < K || lda % 8 != 0 || ldw < K || ldw % 16 != 0 || ldc < N || ldc % 8 != 0) return FGQ_ERR_STRIDE;
+  if (sw_snb < 0 || sw_skb < 0) return FGQ_ERR_STRIDE;
+  if (lda > ((int64_t)1 << 23) || N / 128 > 65535 || M >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
+  if (qa_out) {
+    if (!aligned(qa_out, 16) || !aligned(sa_out, 4)) return FGQ_ERR_ALIGN;
+    if (ldq < K || ldq % 16 != 0 || sa_sm < 0 || sa_skb < 0) return FGQ_ERR_STRIDE;
+  }
+  const size_t need = fgq::gemm_workspace_bytes(M, N, K);
+  if (need > 0) {
+    if (!workspace) return FGQ_ERR_NULL;
+    if (workspace_bytes < need) return FGQ_ERR_SHAPE;
+    if (!aligned(workspace, 256)) return FGQ_ERR_ALIGN;
+  }
+  return from_hip(fgq::launch_gemm_bf16a_fp8_blockscaled(
+      static_cast<const uint16_t*>(a), lda, static_cast<const uint8_t*>(qw), ldw, sw, sw_snb, sw_skb,
+      static_cast<uint16_t*>(c), ldc, M, N, K, mode, static_cast<uint8_t*>(qa_out), ldq, sa_out, sa_sm, sa_skb,
+      workspace, as_stream(stream)));
+}
+
 fgq_status_t fgq_quant_act_1x128_e8m0(const void* x, int64_t ldx, int64_t M, int64_t K, void* q, int64_t ldq,
                                       uint8_t* s, int64_t s_sm, int64_t s_skb, void* stream) {
   const fgq_status_t st = check_act_io(x, ldx, M, K, q, ldq, s, s_sm, s_skb, 1);

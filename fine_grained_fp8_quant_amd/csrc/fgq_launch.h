@@ -70,6 +70,14 @@ hipError_t launch_grouped_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const ui
                                         const int32_t* offsets, int64_t E, int64_t total_rows, uint16_t* c,
                                         int64_t ldc, int64_t N, int64_t K, int in_core, hipStream_t st);
 
+// BF16 activations quantised inside the GEMM's A-load; optional emission of
+// the codes and scales (qa_out == nullptr: none).
+hipError_t launch_gemm_bf16a_fp8_blockscaled(const uint16_t* a, int64_t lda, const uint8_t* qw, int64_t ldw,
+                                             const float* sw, int64_t sw_snb, int64_t sw_skb, uint16_t* c,
+                                             int64_t ldc, int64_t M, int64_t N, int64_t K, int mode,
+                                             uint8_t* qa_out, int64_t ldq, float* sa_out, int64_t sa_sm,
+                                             int64_t sa_skb, void* workspace, hipStream_t st);
+
 hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_debug_mfma(const uint8_t* a, const uint8_t* b, const float* cin, float* d, hipStream_t st);

@@ -525,6 +525,178 @@ using SplitCfg = TileCfg<64, 128, 1, 4, 3>;  // split-K, memory-bound small M: 3
 // pass over their weights) with three stages in flight.
 using MoeDecodeCfg = TileCfg<128, 256, 2, 4, 3>;
 
+// ---------------------------------------------------------------------------
+// Activation quantisation fused into the A-load: the CDNA counterpart of the
+// FP8 cast during the global -> shared transfer that the pages propose (P3
+// paragraph 3), which removes the HBM round trip of quantised activations
+// (P2 paragraph 1).  A arrives as BF16.  Per K chunk each 16-lane group holds
+// one row's 1x128 tile in registers (16 bytes a lane), takes its max-abs,
+// derives the scale pair and codes with the same helpers as
+// k_quant_act_1x128, and writes codes and scale into the LDS stage in the
+// layout the engine reads.  The weights keep their DMA.  With EMIT, the
+// workgroups of n-tile 0 also store the codes and scales to HBM
+// (bit-identical to fgq_quant_act_1x128); HBM stores count in vmcnt on this
+// chip, so that variant waits for all memory operations each chunk.
+template <class C>
+struct FusedA {
+  static constexpr int ROWS_PER_INS = 4;                 // 4 rows of 256 B per wave instruction
+  static constexpr int LOADS = C::BM / (ROWS_PER_INS * C::NW);
+  static constexpr int DMA_PER_CHUNK = C::B_PER_W + 1;   // W slices + one weight-scale (or dummy) load
+  static_assert(C::BM % (ROWS_PER_INS * C::NW) == 0, "whole A rows per thread");
+  static_assert(C::NSTAGE >= 2 && (C::NSTAGE - 2) * DMA_PER_CHUNK <= 63, "vmcnt range");
+};
+
+template <class C, int MODE, bool EMIT, bool PARTIAL = false>
+__device__ __forceinline__ void gemm_tile_fused(const uint16_t* __restrict__ a, int64_t lda, int64_t row_begin,
+                                                int64_t row_end, const uint8_t* __restrict__ qw, int64_t ldw,
+                                                const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
+                                                int64_t n0, uint16_t* __restrict__ c, float* __restrict__ part,
+                                                int64_t ldc, int kb_begin, int kb_end, uint8_t* lds,
+                                                uint8_t* __restrict__ qa_out, int64_t ldq,
+                                                float* __restrict__ sa_out, int64_t sa_sm, int64_t sa_skb) {
+  using F = FusedA<C>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // weight staging as in gemm_tile
+  static_assert(C::NW % 2 == 0, "instruction parity follows the wave's");
+  const int dcol = lds_col(lane & 7, ((wave & 1) << 3) | (lane >> 3)) * 16;
+  const uint8_t* b_tile = qw + n0 * ldw;
+  uint32_t b_src[C::B_PER_W];
+#pragma unroll
+  for (int j = 0; j < C::B_PER_W; ++j) {
+    const int r = (wave + j * C::NW) * 8 + (lane >> 3);
+    b_src[j] = (uint32_t)((r < C::BN ? r : 0) * ldw) + dcol;
+  }
+  const float* sw_src = sw + ((n0 >> 7) + (lane < C::NBW ? lane : 0)) * sw_snb;
+  auto issue_w = [&](int kb, int stage) {
+    uint8_t* base = lds + stage * C::STAGE;
+    const uint8_t* bt = b_tile + (int64_t)kb * 128;
+#pragma unroll
+    for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
+    if (wave == 0) {
+      if (lane < C::NBW) dma4(sw_src + (int64_t)kb * sw_skb, base + C::SW_OFF);
+    } else if (lane == 0) {
+      dma4(sw, base + C::SW_OFF + 128);  // dummy: keeps the per-wave DMA count uniform
+    }
+  };
+
+  // this thread's A rows: tile row (wave + j NW) * 4 + lane / 16, bytes 16 l16 .. of the chunk
+  const uint16_t* a_tile = a + row_begin * lda + l16 * 8;
+  const int64_t a_last = row_end - 1 - row_begin;
+  uint32_t a_off[F::LOADS];
+  int a_row[F::LOADS];
+#pragma unroll
+  for (int j = 0; j < F::LOADS; ++j) {
+    a_row[j] = (wave + j * C::NW) * F::ROWS_PER_INS + (lane >> 4);
+    a_off[j] = (uint32_t)((a_row[j] < a_last ? a_row[j] : a_last) * lda);  // clamped rows: loads stay in bounds
+  }
+  auto load_a = [&](int kb, uint4* v) {
+#pragma unroll
+    for (int j = 0; j < F::LOADS; ++j) v[j] = *reinterpret_cast<const uint4*>(a_tile + a_off[j] + (int64_t)kb * 128);
+  };
+  const bool emit = EMIT && qa_out != nullptr;
+  auto put_a = [&](int kb, const uint4* v, uint8_t* base) {
+#pragma unroll
+    for (int j = 0; j < F::LOADS; ++j) {
+      float f[8];
+      unpack8(v[j], f);
+      const float amax = max16(absmax8(f));
+      float sc, r;
+      group_scales(amax, sc, r);
+      const uint2 codes = cast8(f, r);
+      const int rr = a_row[j];
+      *reinterpret_cast<uint2*>(base + rr * 128 + (lds_col(l16 >> 1, rr) << 4) + (l16 & 1) * 8) = codes;
+      if (l16 == 0) *reinterpret_cast<float*>(base + C::SA_OFF + rr * 4) = sc;
+      if (emit && rr <= a_last) {
+        const int64_t gr = row_begin + rr;
+        *reinterpret_cast<uint2*>(qa_out + gr * ldq + (int64_t)kb * 128 + l16 * 8) = codes;
+        if (l16 == 0) sa_out[gr * sa_sm + (int64_t)kb * sa_skb] = sc;
+      }
+    }
+  };
+
+  Engine16<C, MODE> eng(wave, lane);
+  // A tiles travel two chunks ahead in a two-slot register ring: chunk k
+  // lives in ring[(k - kb_begin) & 1].  Within an iteration the weight
+  // request goes out before the A loads, and the prologue keeps that order,
+  // so at the top of iteration kb the operations issued after the weight
+  // request of chunk kb are exactly the next iteration's: (NSTAGE - 2)
+  // weight requests and one set of A loads (none in the last iteration).
+  static_assert(C::NSTAGE == 2 || C::NSTAGE == 3, "ring and wait counts are laid out for 2 or 3 stages");
+  uint4 ring[2][F::LOADS];
+  if constexpr (C::NSTAGE == 2) {
+    load_a(kb_begin, ring[0]);
+    issue_w(kb_begin, 0);
+    if (kb_begin + 1 < kb_end) load_a(kb_begin + 1, ring[1]);
+  } else {
+    issue_w(kb_begin, 0);
+    load_a(kb_begin, ring[0]);
+    if (kb_begin + 1 < kb_end) {
+      issue_w(kb_begin + 1, 1);
+      load_a(kb_begin + 1, ring[1]);
+    }
+  }
+  put_a(kb_begin, ring[0], lds);
+  constexpr int kAhead = (C::NSTAGE - 2) * F::DMA_PER_CHUNK + F::LOADS;
+  static_assert(kAhead <= 63, "vmcnt range");
+
+  auto step = [&](auto par, int kb) {
+    constexpr int P = decltype(par)::value;  // (kb - kb_begin) & 1
+    const int it = kb - kb_begin;
+    const int stage = it % C::NSTAGE;
+    if (!emit && kb + 1 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(kAhead));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
+    barrier_no_drain();
+    if (kb + C::NSTAGE - 1 < kb_end) issue_w(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
+    if (kb + 2 < kb_end) load_a(kb + 2, ring[P]);  // slot of chunk kb, written to LDS last iteration
+    eng.chunk(lds + stage * C::STAGE, kb);
+    // the next chunk's A goes to the stage every wave finished before this
+    // iteration's barrier
+    if (kb + 1 < kb_end) put_a(kb + 1, ring[P ^ 1], lds + ((it + 1) % C::NSTAGE) * C::STAGE);
+  };
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
+    step(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < kb_end) step(std::integral_constant<int, 1>{}, kb + 1);
+  }
+  eng.template store<PARTIAL>(row_begin, row_end, n0, c, part, ldc);
+}
+
+template <class C, int MODE, bool EMIT>
+__global__ __launch_bounds__(C::NT) void k_gemm_fused_a(const uint16_t* __restrict__ a, int64_t lda,
+                                                        const uint8_t* __restrict__ qw, int64_t ldw,
+                                                        const float* __restrict__ sw, int64_t sw_snb, int64_t sw_skb,
+                                                        uint16_t* __restrict__ c, int64_t ldc, int64_t M, int tiles_m,
+                                                        int KB, uint8_t* __restrict__ qa_out, int64_t ldq,
+                                                        float* __restrict__ sa_out, int64_t sa_sm, int64_t sa_skb) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+  gemm_tile_fused<C, MODE, EMIT>(a, lda, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb, (int64_t)tn * C::BN, c,
+                                 nullptr, ldc, 0, KB, lds, tn == 0 ? qa_out : nullptr, ldq, sa_out, sa_sm, sa_skb);
+}
+
+template <class C, int MODE, bool EMIT>
+__global__ __launch_bounds__(C::NT) void k_gemm_fused_a_splitk(const uint16_t* __restrict__ a, int64_t lda,
+                                                               const uint8_t* __restrict__ qw, int64_t ldw,
+                                                               const float* __restrict__ sw, int64_t sw_snb,
+                                                               int64_t sw_skb, float* __restrict__ part, int64_t M,
+                                                               int64_t N, int tiles_m, int tiles, int KB, int S,
+                                                               uint8_t* __restrict__ qa_out, int64_t ldq,
+                                                               float* __restrict__ sa_out, int64_t sa_sm,
+                                                               int64_t sa_skb) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
+  const int split = blockIdx.x / tiles;
+  int tm, tn;
+  tile_of(blockIdx.x % tiles, tiles, tiles_m, tm, tn);
+  const int kb0 = (int)((int64_t)split * KB / S), kb1 = (int)((int64_t)(split + 1) * KB / S);
+  gemm_tile_fused<C, MODE, EMIT, true>(a, lda, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
+                                       (int64_t)tn * C::BN, nullptr, part + (int64_t)split * M * N, N, kb0, kb1, lds,
+                                       tn == 0 ? qa_out : nullptr, ldq, sa_out, sa_sm, sa_skb);
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict__ qa, int64_t lda,
                                                        const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
@@ -671,6 +843,58 @@ hipError_t launch_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* s
   if (in_core)
     return gemm_dispatch<3>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
   return gemm_dispatch<2>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
+}
+
+// BF16 activations quantised inside the GEMM (see gemm_tile_fused).  Same
+// split plan and workspace as the FP8-operand GEMM; large M uses 128 x 256
+// tiles, which leave the registers for the A tile in flight.
+using FusedBigCfg = TileCfg<128, 256, 2, 4>;
+
+template <int MODE, bool EMIT>
+static void fused_dispatch(const uint16_t* a, int64_t lda, const uint8_t* qw, int64_t ldw, const float* sw,
+                           int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                           void* workspace, uint8_t* qa_out, int64_t ldq, float* sa_out, int64_t sa_sm,
+                           int64_t sa_skb, hipStream_t st) {
+  const SplitPlan p = split_plan(M, N, K);
+  const int KB = (int)(K / 128);
+  if (p.S > 1) {
+    using C = SplitCfg;
+    const int tiles = p.tiles_m * p.tiles_n;
+    float* part = static_cast<float*>(workspace);
+    hipLaunchKernelGGL((k_gemm_fused_a_splitk<C, MODE, EMIT>), dim3(tiles * p.S), dim3(C::NT), 0, st, a, lda, qw, ldw,
+                       sw, sw_snb, sw_skb, part, M, N, p.tiles_m, tiles, KB, p.S, qa_out, ldq, sa_out, sa_sm, sa_skb);
+    const int64_t groups = (M * N + 7) / 8;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, part, p.S, M, N, c,
+                       ldc);
+    return;
+  }
+  if (M > 128 && N % 256 == 0) {
+    using C = FusedBigCfg;
+    const int tiles_m = (int)((M + C::BM - 1) / C::BM);
+    hipLaunchKernelGGL((k_gemm_fused_a<C, MODE, EMIT>), dim3(tiles_m * (int)(N / C::BN)), dim3(C::NT), 0, st, a, lda,
+                       qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, tiles_m, KB, qa_out, ldq, sa_out, sa_sm, sa_skb);
+    return;
+  }
+  using C = SmallCfg;
+  const int tiles_m = (int)((M + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL((k_gemm_fused_a<C, MODE, EMIT>), dim3(tiles_m * (int)(N / C::BN)), dim3(C::NT), 0, st, a, lda, qw,
+                     ldw, sw, sw_snb, sw_skb, c, ldc, M, tiles_m, KB, qa_out, ldq, sa_out, sa_sm, sa_skb);
+}
+
+hipError_t launch_gemm_bf16a_fp8_blockscaled(const uint16_t* a, int64_t lda, const uint8_t* qw, int64_t ldw,
+                                             const float* sw, int64_t sw_snb, int64_t sw_skb, uint16_t* c,
+                                             int64_t ldc, int64_t M, int64_t N, int64_t K, int mode,
+                                             uint8_t* qa_out, int64_t ldq, float* sa_out, int64_t sa_sm,
+                                             int64_t sa_skb, void* workspace, hipStream_t st) {
+  const bool emit = qa_out != nullptr;
+  if (mode == 1) {
+    if (emit) fused_dispatch<1, true>(a, lda, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, qa_out, ldq, sa_out, sa_sm, sa_skb, st);
+    else fused_dispatch<1, false>(a, lda, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, nullptr, 0, nullptr, 0, 0, st);
+  } else {
+    if (emit) fused_dispatch<0, true>(a, lda, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, qa_out, ldq, sa_out, sa_sm, sa_skb, st);
+    else fused_dispatch<0, false>(a, lda, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, nullptr, 0, nullptr, 0, 0, st);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -57,7 +57,7 @@ enum {
   FGQ_ERR_HIP = 6          /* a HIP launch failed; see fgq_last_hip_error() */
 };
 
-#define FGQ_ABI_VERSION 3
+#define FGQ_ABI_VERSION 4
 
 /*
  * fgq_quant_act_1x128 -- online activation quantisation, one scale per
@@ -204,6 +204,37 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
                                               const int32_t* offsets, int64_t E, int64_t total_rows,
                                               void* c, int64_t ldc, int64_t N, int64_t K, int32_t mode,
                                               void* stream);
+
+/*
+ * fgq_gemm_bf16a_fp8_blockscaled -- the 1x128 activation quantisation fused
+ * into the GEMM's A-load.  The pages note that quantised activations make a
+ * round trip through HBM (read as BF16, written as FP8, read again for the
+ * MMA) [P2 paragraph 1] and propose doing the FP8 cast while the activations
+ * move from global memory into shared memory [P3 paragraph 3].  Here the
+ * GEMM reads A in BF16; per 128-wide K chunk each row's tile is quantised in
+ * registers exactly as fgq_quant_act_1x128 does (same codes, same scale),
+ * written to LDS, and multiplied as in fgq_gemm_fp8_blockscaled.  The result
+ * is bit-identical to fgq_quant_act_1x128 followed by
+ * fgq_gemm_fp8_blockscaled with the same mode.
+ *
+ *   a       BF16 [M, K], row stride lda (>= K, multiple of 8, at most 2^23); 16-byte aligned.
+ *   qw, sw, c, M, N, K, mode, workspace: as in fgq_gemm_fp8_blockscaled
+ *           (the same fgq_gemm_workspace_bytes).
+ *   qa_out, sa_out  optional (both NULL or both set): the codes and scales
+ *           of A, written once (by the tiles of the first 128- or 256-column
+ *           block), laid out as fgq_quant_act_1x128's q (row stride ldq,
+ *           16-byte aligned) and s (sa_out[m * sa_sm + kb * sa_skb]).
+ *           Emitting costs time: the GEMM then waits for every memory access
+ *           each chunk.
+ * A is read once per column block of C (from L2 where it fits): this trades
+ * the activation round trip for repeated quantisation work inside the GEMM.
+ */
+fgq_status_t fgq_gemm_bf16a_fp8_blockscaled(const void* a, int64_t lda, const void* qw, int64_t ldw,
+                                            const float* sw, int64_t sw_snb, int64_t sw_skb, void* c,
+                                            int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t mode,
+                                            void* qa_out, int64_t ldq, float* sa_out, int64_t sa_sm,
+                                            int64_t sa_skb, void* workspace, size_t workspace_bytes,
+                                            void* stream);
 
 /*
  * fgq_quant_dispatch_1x128 -- quantise-then-dispatch: the activations that

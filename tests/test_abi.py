@@ -34,7 +34,8 @@ def test_header_declares_the_five_calls():
     for n in ("fgq_quant_act_1x128", "fgq_quant_w_128x128", "fgq_fused_rmsnorm_quant",
               "fgq_gemm_fp8_blockscaled", "fgq_grouped_gemm_fp8_blockscaled", "fgq_quant_dispatch_1x128",
               "fgq_quant_act_1x128_e8m0", "fgq_quant_w_128x128_e8m0", "fgq_fused_rmsnorm_quant_e8m0",
-              "fgq_gemm_fp8_e8m0", "fgq_grouped_gemm_fp8_e8m0", "fgq_quant_dispatch_1x128_e8m0"):
+              "fgq_gemm_fp8_e8m0", "fgq_grouped_gemm_fp8_e8m0", "fgq_quant_dispatch_1x128_e8m0",
+              "fgq_gemm_bf16a_fp8_blockscaled"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fgq_abi_version() == 3
+    assert lib.fgq_abi_version() == 4
     for code in range(7):
         assert lib.fgq_status_string(code)
     assert lib.fgq_status_string(99) == b"unknown status"
@@ -271,3 +272,28 @@ def test_dispatch_e8m0_validation(lib):
     assert call(off=0) == NULL
     assert call(ldq=128) == STRIDE          # an odd scale address passes the alignment check
     assert dispatch(lib, s=S + 1025, ldq=128) == ALIGN
+
+
+def gemm16(lib, a=P, lda=256, qw=Q, ldw=256, sw=S, sw_snb=2, sw_skb=1, c=Q, ldc=256, M=4, N=256, K=256, mode=0,
+           qa=0, ldq=256, sa=0, sa_sm=2, sa_skb=1, ws=0, ws_bytes=0):
+    return lib.fgq_gemm_bf16a_fp8_blockscaled(a, lda, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, mode, qa, ldq,
+                                              sa, sa_sm, sa_skb, ws, ws_bytes, None)
+
+
+def test_gemm_bf16a_validation(lib):
+    assert gemm16(lib, M=-1) == SHAPE
+    assert gemm16(lib, mode=2) == UNSUP
+    assert gemm16(lib, K=200) == UNSUP
+    assert gemm16(lib, M=0) == OK
+    assert gemm16(lib, a=0) == NULL
+    assert gemm16(lib, qa=Q) == NULL                 # codes without scales
+    assert gemm16(lib, sa=S) == NULL                 # scales without codes
+    assert gemm16(lib, a=P + 8) == ALIGN
+    assert gemm16(lib, qa=Q + 8, sa=S) == ALIGN
+    assert gemm16(lib, lda=128) == STRIDE
+    assert gemm16(lib, lda=260) == STRIDE
+    assert gemm16(lib, qa=Q, sa=S, ldq=264) == STRIDE
+    assert gemm16(lib, lda=(1 << 23) + 8, K=256) == UNSUP
+    need = lib.fgq_gemm_workspace_bytes(64, 18432, 7168)
+    assert gemm16(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL      # no workspace
+    assert gemm16(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
