@@ -129,9 +129,13 @@ constexpr int waitcnt_vm_lds(int n) { return (n & 15) | ((n >> 4) << 14) | (7 <<
 // keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void barrier_no_drain() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_ = 2>
+// SKIP: the tile's waves all span its rows (WAVES_M = 1), so a tile with
+// fewer rows than BM runs only the 16-row sub-tiles that hold rows (in
+// quarter steps, chosen once per workgroup).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_ = 2, bool SKIP_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NSTAGE = NSTAGE_;
+  static constexpr bool SKIP = SKIP_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
@@ -153,6 +157,7 @@ struct TileCfg {
   static_assert(WN <= 128 && (128 % WN == 0), "a wave's columns share one weight-scale block");
   static_assert(SA_INS + 1 <= NW, "scale loads need a wave each");
   static_assert(NBW <= 64, "weight scales fit one instruction");
+  static_assert(!SKIP || (WAVES_M == 1 && TM % 4 == 0), "row skipping needs full-height waves");
 };
 
 // Physical 16-byte column of logical column c in LDS row r.  A fragment read
@@ -203,13 +208,16 @@ struct Engine16 {
     sw_idx = (wn * C::WN) / 128;
   }
 
+  // TMA: sub-tile rows that hold rows of the tile (the rest are skipped)
+  template <int TMA = C::TM>
   __device__ __forceinline__ void chunk(const uint8_t* base, int kb) {
-    if constexpr (MODE >= 2) chunk_e8m0(base, kb);
-    else chunk_f32(base);
+    if constexpr (MODE >= 2) chunk_e8m0<TMA>(base, kb);
+    else chunk_f32<TMA>(base);
   }
 
   // E8M0: one scale byte per sub-tile row (this lane's row l16) and one per
   // wave for the weights; the unit multiplies them in
+  template <int TMA>
   __device__ __forceinline__ void chunk_e8m0(const uint8_t* base, int kb) {
     const int swv = base[C::SW_OFF + sw_idx * 4 + ((sw_lo + (uint32_t)kb * sw_step) & 3u)];
     const int a_byte = sa_off + (int)((sa_lo + (uint32_t)kb * sa_step) & 3u);
@@ -228,10 +236,10 @@ struct Engine16 {
     // operation that produces its input
     v4f tp[C::TN];
 #pragma unroll
-    for (int mi = 0; mi < C::TM; ++mi) {
+    for (int mi = 0; mi < TMA; ++mi) {
       uint4 nlo = alo, nhi = ahi;
       int nsa = sav;
-      if (mi + 1 < C::TM) {
+      if (mi + 1 < TMA) {
         nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
         nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
         nsa = base[a_byte + (mi + 1) * 64];
@@ -261,7 +269,7 @@ struct Engine16 {
     }
     if constexpr (MODE == 2) {
 #pragma unroll
-      for (int ni = 0; ni < C::TN; ++ni) add4(acc[C::TM - 1][ni], tp[ni]);
+      for (int ni = 0; ni < C::TN; ++ni) add4(acc[TMA - 1][ni], tp[ni]);
     }
   }
 
@@ -282,6 +290,7 @@ struct Engine16 {
   }
 
   // binary32 scales: the chunk's FP32 sum, then promotion by the vector ALU
+  template <int TMA>
   __device__ __forceinline__ void chunk_f32(const uint8_t* base) {
     const float swv = reinterpret_cast<const float*>(base + C::SW_OFF)[sw_idx];
     if constexpr (MODE == 1) {
@@ -301,10 +310,10 @@ struct Engine16 {
       v4f tp[C::TN];
       v4f sp;
 #pragma unroll
-      for (int mi = 0; mi < C::TM; ++mi) {
+      for (int mi = 0; mi < TMA; ++mi) {
         uint4 nlo = alo, nhi = ahi;
         v4f nsa = sa4;
-        if (mi + 1 < C::TM) {
+        if (mi + 1 < TMA) {
           nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
           nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
           nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
@@ -327,7 +336,7 @@ struct Engine16 {
         sa4 = nsa;
       }
 #pragma unroll
-      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[C::TM - 1][ni], tp[ni], sp);
+      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], tp[ni], sp);
     } else {
       // exact products: codes -> FP16 in registers, four K = 32 steps per chunk
       v8h bh[C::TN][4];
@@ -344,10 +353,10 @@ struct Engine16 {
       uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
       v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
 #pragma unroll
-      for (int mi = 0; mi < C::TM; ++mi) {
+      for (int mi = 0; mi < TMA; ++mi) {
         uint4 nlo = alo, nhi = ahi;
         v4f nsa = sa4;
-        if (mi + 1 < C::TM) {
+        if (mi + 1 < TMA) {
           nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
           nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
           nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
@@ -486,14 +495,26 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
 #pragma unroll
   for (int p = 0; p < C::NSTAGE - 1; ++p)
     if (kb_begin + p < kb_end) issue(kb_begin + p, p);
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const int it = kb - kb_begin;
-    const int stage = it % C::NSTAGE;
-    if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
-    barrier_no_drain();
-    if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-    eng.chunk(lds + stage * C::STAGE, kb);
+  auto kloop = [&](auto tma) {
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+      const int it = kb - kb_begin;
+      const int stage = it % C::NSTAGE;
+      if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
+      barrier_no_drain();
+      if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
+      eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
+    }
+  };
+  if constexpr (C::SKIP) {
+    // sub-tile rows past the tile's last row hold no rows: skip them
+    const int64_t rows = row_end - row_begin;
+    if (rows <= C::BM / 4) kloop(std::integral_constant<int, C::TM / 4>{});
+    else if (rows <= C::BM / 2) kloop(std::integral_constant<int, C::TM / 2>{});
+    else if (rows <= 3 * C::BM / 4) kloop(std::integral_constant<int, 3 * C::TM / 4>{});
+    else kloop(std::integral_constant<int, C::TM>{});
+  } else {
+    kloop(std::integral_constant<int, C::TM>{});
   }
   eng.template store<PARTIAL>(row_begin, row_end, n0, c, part, ldc);
 }
@@ -521,9 +542,11 @@ using BigExactCfg = TileCfg<192, 256, 2, 4>; // exact products, large M (FP16 op
 using SmallCfg = TileCfg<64, 128, 1, 4>;
 using SplitCfg = TileCfg<64, 128, 1, 4, 3>;  // split-K, memory-bound small M: 3 stages, 2 per CU
 // Grouped GEMM with few rows per expert (decode batches): the expert weights
-// dominate the traffic; 128-row tiles hold most experts in one slot (one
-// pass over their weights) with three stages in flight.
-using MoeDecodeCfg = TileCfg<128, 256, 2, 4, 3>;
+// dominate the traffic.  64 x 128 tiles with full-height waves: a slot runs
+// only the 16-row sub-tiles that hold rows, and two stages (49 KB of LDS)
+// leave room for three workgroups per CU; the slots of one expert share each
+// weight column block in L2 (tile_of keeps them together).
+using MoeDecodeCfg = TileCfg<64, 128, 1, 4, 2, true>;
 
 // ---------------------------------------------------------------------------
 // Activation quantisation fused into the A-load: the CDNA counterpart of the
