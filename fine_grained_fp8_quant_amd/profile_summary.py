@@ -42,9 +42,12 @@ def sha(rel):
 def short(name: str) -> str:
     """Kernel display name without the argument list, with the GEMM mode spelled out."""
     base = name.split("(")[0].replace("void ", "").replace("fgq::", "")
-    m = re.match(r"(k_\w+)<TileCfg<(\d+), (\d+), (\d+), (\d+)(?:, (\d+))?>, (\d)>", base)
+    # k_name<TileCfg<BM, BN, waves_m, waves_n[, stages][, skip]>, mode[, emit]>
+    m = re.match(r"(k_\w+)<TileCfg<(\d+), (\d+), \d+, \d+(?:, \d+)?(?:, (?:true|false))?>, (\d)(, true|, false)?>",
+                 base)
     if m:
-        return f"{m.group(1)}[{m.group(2)}x{m.group(3)},{MODE_NAMES[m.group(7)]}]"
+        emit = ",emit" if m.group(5) == ", true" else ""
+        return f"{m.group(1)}[{m.group(2)}x{m.group(3)},{MODE_NAMES[m.group(4)]}{emit}]"
     return base
 
 
@@ -61,7 +64,9 @@ def api_of(kname: str, e8: bool):
         return "fused_rmsnorm_quant" + sfx, None
     if kname.startswith("k_dispatch"):
         return "quant_dispatch_1x128" + sfx, None
-    mode = next((m for m in MODE_NAMES.values() if "," + m + "]" in kname), None)
+    mode = next((m for m in MODE_NAMES.values() if "," + m + "]" in kname or "," + m + "," in kname), None)
+    if kname.startswith("k_gemm_fused_a"):
+        return "gemm_bf16a_fp8_blockscaled", mode
     if kname.startswith("k_grouped"):
         return ("grouped_gemm_fp8_e8m0" if e8 else "grouped_gemm_fp8_blockscaled"), mode
     if kname.startswith("k_gemm") or kname.startswith("k_splitk"):
