@@ -925,7 +925,8 @@ hipError_t launch_gemm_bf16a_fp8_blockscaled(const uint16_t* a, int64_t lda, con
 // (m-tile slot, n-tile) pair; slots run over all experts in expert order.
 // The slot -> (expert, rows) map is computed on the GPU from offsets[] with
 // a workgroup-wide prefix sum over the per-expert tile counts, so the host
-// never reads the routing result.  Slots past the last real tile leave at once.
+// never reads the routing result.  The grid is sized for the most slots the
+// sizes allow; workgroups beyond the real tiles leave at once.
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
     const uint8_t* __restrict__ qa, int64_t lda, const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
@@ -936,22 +937,42 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
   int* scan = reinterpret_cast<int*>(lds);  // reused before the tile loop starts
   __shared__ int found[3];
+  __shared__ int wave_tiles[C::NW];
   const int tid = threadIdx.x;
-  int slot, tn;
-  tile_of(blockIdx.x, gridDim.x, slots, slot, tn);
+  // expert e's rows, clamped to [0, total_rows), and its number of row slots
+  auto expert_tiles = [&](int e, int64_t& r0, int64_t& r1) {
+    r0 = offsets[e];
+    r1 = offsets[e + 1];
+    r0 = r0 < 0 ? 0 : (r0 > total_rows ? total_rows : r0);
+    r1 = r1 < r0 ? r0 : (r1 > total_rows ? total_rows : r1);
+    return (int)((r1 - r0 + C::BM - 1) / C::BM);
+  };
+  // The real number of row slots first: workgroup ids are dealt over the
+  // real tiles only, so they spread evenly over the XCDs and the
+  // launch-size bound's spare slots do not leave a partial last round.
+  int mine = 0;
+  for (int e = tid; e < E; e += C::NT) {
+    int64_t r0, r1;
+    mine += expert_tiles(e, r0, r1);
+  }
+  for (int d = 32; d >= 1; d >>= 1) mine += __shfl_xor(mine, d);
+  if ((tid & 63) == 0) wave_tiles[tid >> 6] = mine;
   if (tid == 0) found[0] = -1;
+  __syncthreads();
+  int real_slots = 0;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) real_slots += wave_tiles[w];
+  const int tiles_n = (int)gridDim.x / slots;
+  const int G = real_slots * tiles_n;
+  if ((int)blockIdx.x >= G) return;  // no tile left for this workgroup (the whole workgroup leaves)
+  int slot, tn;
+  tile_of(blockIdx.x, G, real_slots, slot, tn);
   int carried = 0;  // tiles of the experts before this batch
   for (int e0 = 0; e0 < E; e0 += C::NT) {
     const int e = e0 + tid;
     int tiles = 0;
     int64_t r0 = 0, r1 = 0;
-    if (e < E) {
-      r0 = offsets[e];
-      r1 = offsets[e + 1];
-      r0 = r0 < 0 ? 0 : (r0 > total_rows ? total_rows : r0);
-      r1 = r1 < r0 ? r0 : (r1 > total_rows ? total_rows : r1);
-      tiles = (int)((r1 - r0 + C::BM - 1) / C::BM);
-    }
+    if (e < E) tiles = expert_tiles(e, r0, r1);
     scan[tid] = tiles;
     __syncthreads();
     for (int d = 1; d < C::NT; d <<= 1) {  // inclusive Hillis-Steele scan
@@ -972,9 +993,12 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
     if (found[0] >= 0 || slot < carried) break;
   }
   __syncthreads();
-  const int e = found[0];
+  // the same for every lane: say so, so that the addresses built from them
+  // stay scalar as in the dense kernel
+  const int e = __builtin_amdgcn_readfirstlane(found[0]);
   if (e < 0) return;  // slot past the last tile: the whole workgroup leaves
-  const int64_t row_begin = found[1], row_end = found[2];
+  const int64_t row_begin = __builtin_amdgcn_readfirstlane(found[1]);
+  const int64_t row_end = __builtin_amdgcn_readfirstlane(found[2]);
   gemm_tile<C, MODE>(qa, lda, sa, sa_sm, sa_skb, row_begin, row_end, qw + (int64_t)e * w_es, ldw,
                      sw + (int64_t)e * sw_es, sw_snb, sw_skb, (int64_t)tn * C::BN, c, nullptr, ldc, 0, KB, lds);
 }
