@@ -935,70 +935,60 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
     const int32_t* __restrict__ offsets, int E, int64_t total_rows, uint16_t* __restrict__ c,
     int64_t ldc, int slots, int KB) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
-  int* scan = reinterpret_cast<int*>(lds);  // reused before the tile loop starts
-  __shared__ int found[3];
-  __shared__ int wave_tiles[C::NW];
-  const int tid = threadIdx.x;
-  // expert e's rows, clamped to [0, total_rows), and its number of row slots
-  auto expert_tiles = [&](int e, int64_t& r0, int64_t& r1) {
-    r0 = offsets[e];
-    r1 = offsets[e + 1];
-    r0 = r0 < 0 ? 0 : (r0 > total_rows ? total_rows : r0);
-    r1 = r1 < r0 ? r0 : (r1 > total_rows ? total_rows : r1);
-    return (int)((r1 - r0 + C::BM - 1) / C::BM);
-  };
-  // The real number of row slots first: workgroup ids are dealt over the
-  // real tiles only, so they spread evenly over the XCDs and the
-  // launch-size bound's spare slots do not leave a partial last round.
-  int mine = 0;
-  for (int e = tid; e < E; e += C::NT) {
-    int64_t r0, r1;
-    mine += expert_tiles(e, r0, r1);
-  }
-  for (int d = 32; d >= 1; d >>= 1) mine += __shfl_xor(mine, d);
-  if ((tid & 63) == 0) wave_tiles[tid >> 6] = mine;
-  if (tid == 0) found[0] = -1;
-  __syncthreads();
-  int real_slots = 0;
+  // Every wave resolves the tile by itself on the scalar unit: the offsets
+  // are read with uniform addresses (scalar loads through the scalar cache),
+  // with no LDS and no barrier, so each wave starts its first requests as
+  // soon as it can.  (A workgroup-wide scan here cost about 15%: workgroups
+  // started unevenly and lost the L2 sharing of their neighbours.)
+  constexpr int kBatch = 16;  // experts per batch of scalar loads
+  // slots of expert e0 + j from the batch o[0..kBatch], rows clamped to [0, total_rows)
+  auto batch = [&](int e0, int32_t* o) {
 #pragma unroll
-  for (int w = 0; w < C::NW; ++w) real_slots += wave_tiles[w];
+    for (int j = 0; j <= kBatch; ++j) o[j] = offsets[e0 + j < E ? e0 + j : E];
+  };
+  const int32_t nrows = (int32_t)total_rows;  // < 2^31 (checked on the host)
+  auto clamp_rows = [&](int32_t a, int32_t b, int32_t& r0, int32_t& r1) {
+    r0 = a < 0 ? 0 : (a > nrows ? nrows : a);
+    r1 = b < r0 ? r0 : (b > nrows ? nrows : b);
+    return (int)((uint32_t)(r1 - r0 + C::BM - 1) / (uint32_t)C::BM);
+  };
+  // the real number of row slots first: workgroup ids are dealt over the
+  // real tiles only, so they spread evenly over the XCDs and the
+  // launch-size bound's spare slots do not leave a partial last round
+  int real_slots = 0;
+  for (int e0 = 0; e0 < E; e0 += kBatch) {
+    int32_t o[kBatch + 1];
+    batch(e0, o);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      int32_t r0, r1;
+      if (e0 + j < E) real_slots += clamp_rows(o[j], o[j + 1], r0, r1);
+    }
+  }
   const int tiles_n = (int)gridDim.x / slots;
   const int G = real_slots * tiles_n;
-  if ((int)blockIdx.x >= G) return;  // no tile left for this workgroup (the whole workgroup leaves)
+  if ((int)blockIdx.x >= G) return;  // no tile for this workgroup: the whole workgroup leaves
   int slot, tn;
   tile_of(blockIdx.x, G, real_slots, slot, tn);
-  int carried = 0;  // tiles of the experts before this batch
-  for (int e0 = 0; e0 < E; e0 += C::NT) {
-    const int e = e0 + tid;
-    int tiles = 0;
-    int64_t r0 = 0, r1 = 0;
-    if (e < E) tiles = expert_tiles(e, r0, r1);
-    scan[tid] = tiles;
-    __syncthreads();
-    for (int d = 1; d < C::NT; d <<= 1) {  // inclusive Hillis-Steele scan
-      const int v = tid >= d ? scan[tid - d] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
+  int e = -1;
+  int64_t row_begin = 0, row_end = 0;
+  int carried = 0;  // slots of the experts before e0 + j
+  for (int e0 = 0; e0 < E && e < 0; e0 += kBatch) {
+    int32_t o[kBatch + 1];
+    batch(e0, o);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      int32_t r0 = 0, r1 = 0;
+      const int t = e0 + j < E ? clamp_rows(o[j], o[j + 1], r0, r1) : 0;
+      if (e < 0 && slot < carried + t) {
+        e = e0 + j;
+        row_begin = r0 + (int64_t)(slot - carried) * C::BM;
+        row_end = r1;
+      }
+      carried += t;
     }
-    const int incl = carried + scan[tid];
-    const int excl = incl - tiles;
-    if (tiles > 0 && slot >= excl && slot < incl) {
-      found[0] = e;
-      found[1] = (int)(r0 + (int64_t)(slot - excl) * C::BM);
-      found[2] = (int)r1;
-    }
-    carried += scan[C::NT - 1];
-    __syncthreads();
-    if (found[0] >= 0 || slot < carried) break;
   }
-  __syncthreads();
-  // the same for every lane: say so, so that the addresses built from them
-  // stay scalar as in the dense kernel
-  const int e = __builtin_amdgcn_readfirstlane(found[0]);
-  if (e < 0) return;  // slot past the last tile: the whole workgroup leaves
-  const int64_t row_begin = __builtin_amdgcn_readfirstlane(found[1]);
-  const int64_t row_end = __builtin_amdgcn_readfirstlane(found[2]);
+  if (e < 0) return;  // unreachable for slot < real_slots
   gemm_tile<C, MODE>(qa, lda, sa, sa_sm, sa_skb, row_begin, row_end, qw + (int64_t)e * w_es, ldw,
                      sw + (int64_t)e * sw_es, sw_snb, sw_skb, (int64_t)tn * C::BN, c, nullptr, ldc, 0, KB, lds);
 }
