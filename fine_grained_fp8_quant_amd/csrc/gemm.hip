@@ -30,7 +30,7 @@
 //     layout, so whatever order the unit pairs the 128 K positions in, the
 //     sum is the full chunk dot product.
 //   * LDS rows are 128 bytes (one chunk); the 16-byte column c of row r is
-//     stored at column c ^ ((r / 2) mod 8), which keeps the fragment reads
+//     stored at column c ^ s(r), a swizzle that keeps the fragment reads
 //     (16 consecutive rows at one logical column) free of bank conflicts.
 //   * Staging is LDS DMA (global_load_lds, no registers) into NSTAGE stages:
 //     chunk kb + NSTAGE - 1 is in flight while chunk kb is multiplied.  The
@@ -160,12 +160,16 @@ struct TileCfg {
   static_assert(!SKIP || (WAVES_M == 1 && TM % 4 == 0), "row skipping needs full-height waves");
 };
 
-// Physical 16-byte column of logical column c in LDS row r.  A fragment read
-// has 16 lanes on 16 consecutive rows at one logical column; rows are 128
-// bytes (32 of the 64 four-byte banks), so rows r and r + 2 share banks
-// unless their columns differ: XOR with (r / 2) mod 8 spreads the 16 rows
-// over all 64 banks.
-__device__ __forceinline__ int lds_col(int c, int r) { return c ^ ((r >> 1) & 7); }
+// Physical 16-byte column of logical column c in LDS row r.  gfx950's LDS
+// serves a 16-byte-per-lane read in two halves of 32 lanes, each over 128
+// four-byte banks (512 bytes), so the 32 addresses of a half must fall in 32
+// different 16-byte slots modulo 512 bytes (measured: the rate halves
+// otherwise).  A fragment read's half holds rows r = 0 .. 15 (mod 16) at
+// logical columns c and c ^ 2; its slot is 8 (r mod 4) + physical column.
+// For each r mod 4 the four rows' physical columns c ^ s and c ^ 2 ^ s must
+// cover 0 .. 7, which s(r) in {0, 1, 4, 5} (bits 2 and 3 of r) does.  s
+// depends only on r mod 16, and c -> c ^ s is its own inverse.
+__device__ __forceinline__ int lds_col(int c, int r) { return c ^ (((r >> 2) & 1) | ((r >> 1) & 4)); }
 
 // ---- per-chunk arithmetic of one wave.  An engine holds the wave's
 // accumulators; chunk() multiplies the K chunk staged at `base` (layout of
