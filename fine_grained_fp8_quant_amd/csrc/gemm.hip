@@ -160,16 +160,17 @@ struct TileCfg {
   static_assert(!SKIP || (WAVES_M == 1 && TM % 4 == 0), "row skipping needs full-height waves");
 };
 
-// Physical 16-byte column of logical column c in LDS row r.  gfx950's LDS
-// serves a 16-byte-per-lane read in two halves of 32 lanes, each over 128
-// four-byte banks (512 bytes), so the 32 addresses of a half must fall in 32
-// different 16-byte slots modulo 512 bytes (measured: the rate halves
-// otherwise).  A fragment read's half holds rows r = 0 .. 15 (mod 16) at
-// logical columns c and c ^ 2; its slot is 8 (r mod 4) + physical column.
-// For each r mod 4 the four rows' physical columns c ^ s and c ^ 2 ^ s must
-// cover 0 .. 7, which s(r) in {0, 1, 4, 5} (bits 2 and 3 of r) does.  s
-// depends only on r mod 16, and c -> c ^ s is its own inverse.
-__device__ __forceinline__ int lds_col(int c, int r) { return c ^ (((r >> 2) & 1) | ((r >> 1) & 4)); }
+// Physical 16-byte column of logical column c in LDS row r.  Measured on
+// gfx950: a 16-byte-per-lane LDS read runs at full rate (256 B/clk per CU)
+// only when its 64 lanes fall in 64 different 16-byte slots modulo 1 KB.  A
+// fragment read has rows r = 0 .. 15 (mod 16) at logical columns 2 g + h
+// (g = 0 .. 3, h fixed); with 128-byte rows its slot is 8 (r mod 8) + the
+// physical column, so rows r and r + 8 must share the eight physical columns
+// between them.  Swizzle s(r) = (bit 3 of r) | (r & 6) does it (bit 0 of s
+// differs between r and r + 8); c ^ (r / 2 mod 8), whose bit 0 does not,
+// measured 142 B/clk.  s depends only on r mod 16, and c -> c ^ s is its own
+// inverse.
+__device__ __forceinline__ int lds_col(int c, int r) { return c ^ (((r >> 3) & 1) | (r & 6)); }
 
 // ---- per-chunk arithmetic of one wave.  An engine holds the wave's
 // accumulators; chunk() multiplies the K chunk staged at `base` (layout of
