@@ -238,7 +238,7 @@ def make_step(args, fgq, d, n_sets, mode):
             o["off"] = torch.empty(E + 1, dtype=torch.int32, device="cuda")
             o["src"] = torch.empty(R, dtype=torch.int32, device="cuda")
             o["dest"] = torch.empty(R, dtype=torch.int32, device="cuda")
-            o["dws"] = torch.empty(max(fgq.quant_dispatch_workspace_bytes(T, topk, E), 1), dtype=torch.uint8,
+            o["dws"] = torch.empty(max(fgq.quant_dispatch_workspace_bytes(T, topk, E, K), 1), dtype=torch.uint8,
                                    device="cuda")
             o["qw"] = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
             o["sw"] = torch.empty((E, N // 128, K // 128), dtype=sdt, device="cuda")

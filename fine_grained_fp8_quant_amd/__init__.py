@@ -88,7 +88,7 @@ _SIGNATURES = {
     "fgq_gemm_workspace_bytes": [_i64, _i64, _i64],
     "fgq_quant_dispatch_1x128": [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                  _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
-    "fgq_quant_dispatch_workspace_bytes": [_i64, _i64, _i64],
+    "fgq_quant_dispatch_workspace_bytes": [_i64, _i64, _i64, _i64],
     "fgq_status_string": [_st],
     "fgq_last_hip_error": [],
     "fgq_abi_version": [],
@@ -291,9 +291,9 @@ def fused_rmsnorm_quant_e8m0(x, gamma, eps: float, q=None, s=None, stream=None):
     return _fused(lib.fgq_fused_rmsnorm_quant_e8m0, _torch().uint8, x, gamma, eps, q, s, stream)
 
 
-def quant_dispatch_workspace_bytes(T: int, topk: int, E: int) -> int:
+def quant_dispatch_workspace_bytes(T: int, topk: int, E: int, K: int) -> int:
     load_library()
-    return int(lib.fgq_quant_dispatch_workspace_bytes(T, topk, E))
+    return int(lib.fgq_quant_dispatch_workspace_bytes(T, topk, E, K))
 
 
 def quant_dispatch_1x128(x, ids, n_experts: int, q=None, s=None, offsets=None, row_src=None, dest=None,
@@ -338,7 +338,7 @@ def _dispatch(fn, sdtype, x, ids, n_experts, q, s, offsets, row_src, dest, works
         row_src = torch.empty(R, dtype=torch.int32, device=dev)
     if dest is None:
         dest = torch.empty(R, dtype=torch.int32, device=dev)
-    need = quant_dispatch_workspace_bytes(T, topk, n_experts)
+    need = quant_dispatch_workspace_bytes(T, topk, n_experts, K)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

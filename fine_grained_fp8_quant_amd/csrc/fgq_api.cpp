@@ -305,7 +305,7 @@ fgq_status_t check_dispatch(const void* x, int64_t ldx, int64_t T, int64_t K, co
                             const int32_t* offsets, const int32_t* row_src, const int32_t* dest,
                             const void* workspace, size_t workspace_bytes, uintptr_t s_align) {
   if (T < 0 || K < 0 || topk < 1 || E < 1) return FGQ_ERR_SHAPE;
-  if (K % 128 != 0 || E > 4096) return FGQ_ERR_UNSUPPORTED;
+  if (K % 128 != 0 || E > 4096 || K / 128 > 65535) return FGQ_ERR_UNSUPPORTED;
   if (T >= kMaxTiles || topk >= kMaxTiles || T * topk >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
   if (!offsets) return FGQ_ERR_NULL;
   if (!aligned(offsets, 4)) return FGQ_ERR_ALIGN;
@@ -314,7 +314,7 @@ fgq_status_t check_dispatch(const void* x, int64_t ldx, int64_t T, int64_t K, co
     if (!aligned(ids, 4) || !aligned(row_src, 4) || !aligned(dest, 4)) return FGQ_ERR_ALIGN;
     const fgq_status_t st = check_act_io(x, ldx, T, K, q, ldq, s, s_sm, s_skb, s_align);
     if (st != FGQ_OK) return st;
-    const size_t need = fgq::dispatch_workspace_bytes(T, topk, E);
+    const size_t need = fgq::dispatch_workspace_bytes(T, topk, E, K);
     if (need > 0) {
       if (!workspace) return FGQ_ERR_NULL;
       if (workspace_bytes < need) return FGQ_ERR_SHAPE;
@@ -352,9 +352,10 @@ fgq_status_t fgq_quant_dispatch_1x128_e8m0(const void* x, int64_t ldx, int64_t T
                                                         row_src, dest, workspace, as_stream(stream)));
 }
 
-size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E) {
-  if (T < 0 || topk < 1 || E < 1 || T >= kMaxTiles || topk >= kMaxTiles || T * topk >= kMaxTiles) return 0;
-  return fgq::dispatch_workspace_bytes(T, topk, E);
+size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t K) {
+  if (T < 0 || topk < 1 || E < 1 || K < 0 || K % 128 != 0) return 0;
+  if (T >= kMaxTiles || topk >= kMaxTiles || T * topk >= kMaxTiles || T * (K / 128) >= kMaxTiles) return 0;
+  return fgq::dispatch_workspace_bytes(T, topk, E, K);
 }
 
 int32_t fgq_abi_version(void) { return FGQ_ABI_VERSION; }

@@ -40,7 +40,7 @@ hipError_t launch_quant_dispatch_1x128(const uint16_t* x, int64_t ldx, int64_t T
                                        float* s, int64_t s_sm, int64_t s_skb, int32_t* offsets,
                                        int32_t* row_src, int32_t* dest, void* workspace, hipStream_t st);
 
-size_t dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+size_t dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t K);
 
 // Power-of-two (E8M0 byte) scale variants of the quantisers and GEMMs.
 hipError_t launch_quant_act_1x128_e8m0(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q,

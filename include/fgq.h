@@ -57,7 +57,7 @@ enum {
   FGQ_ERR_HIP = 6          /* a HIP launch failed; see fgq_last_hip_error() */
 };
 
-#define FGQ_ABI_VERSION 4
+#define FGQ_ABI_VERSION 5
 
 /*
  * fgq_quant_act_1x128 -- online activation quantisation, one scale per
@@ -266,10 +266,16 @@ fgq_status_t fgq_gemm_bf16a_fp8_blockscaled(const void* a, int64_t lda, const vo
  *   row_src  DEVICE int32 [T * topk] output; entries >= R are not written.
  *   dest     DEVICE int32 [T * topk] output.
  *   workspace / workspace_bytes: scratch the caller provides; at least
- *            fgq_quant_dispatch_workspace_bytes(T, topk, E) bytes, 256-byte
- *            aligned (may be NULL when that is 0).
- *   K a multiple of 128; T >= 0; topk >= 1; 1 <= E <= 4096;
- *   T * topk < 2^31.  The inputs are read only by the GPU (no host sync).
+ *            fgq_quant_dispatch_workspace_bytes(T, topk, E, K) bytes,
+ *            256-byte aligned (may be NULL when that is 0).  It holds the
+ *            routing counts and, when a row's scales are not contiguous
+ *            (s_skb != 1, e.g. the K-block-major layout the GEMM reads
+ *            best), one scale per token tile: those are then written once
+ *            per token and copied to the routed rows in row order, instead
+ *            of being stored 4-byte by 4-byte to scattered rows.
+ *   K a multiple of 128 with K / 128 <= 65535; T >= 0; topk >= 1;
+ *   1 <= E <= 4096; T * topk < 2^31.  The inputs are read only by the GPU
+ *   (no host sync).
  */
 fgq_status_t fgq_quant_dispatch_1x128(const void* x, int64_t ldx, int64_t T, int64_t K,
                                       const int32_t* ids, int64_t topk, int64_t E, void* q,
@@ -277,8 +283,9 @@ fgq_status_t fgq_quant_dispatch_1x128(const void* x, int64_t ldx, int64_t T, int
                                       int32_t* offsets, int32_t* row_src, int32_t* dest,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace fgq_quant_dispatch_1x128 needs (0 = none). */
-size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+/* Bytes of workspace fgq_quant_dispatch_1x128 (and its E8M0 variant) needs
+ * (0 = none, or arguments out of range). */
+size_t fgq_quant_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t K);
 
 /*
  * Power-of-two (E8M0) scales.  The pages note that per-group scaling along K

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fgq_abi_version() == 4
+    assert lib.fgq_abi_version() == 5
     for code in range(7):
         assert lib.fgq_status_string(code)
     assert lib.fgq_status_string(99) == b"unknown status"
@@ -189,6 +189,7 @@ def test_dispatch_validation(lib):
     assert dispatch(lib, E=0) == SHAPE
     assert dispatch(lib, E=4097) == UNSUP
     assert dispatch(lib, K=200) == UNSUP
+    assert dispatch(lib, K=128 * 65536) == UNSUP     # K / 128 beyond the scale gather's grid
     assert dispatch(lib, T=1 << 20, topk=1 << 12) == UNSUP      # 2^32 pairs
     assert dispatch(lib, off=0) == NULL
     assert dispatch(lib, off=S + 2050) == ALIGN
@@ -199,14 +200,18 @@ def test_dispatch_validation(lib):
     assert dispatch(lib, q=0) == NULL
     assert dispatch(lib, ldq=128) == STRIDE
     assert dispatch(lib, s_skb=-1) == STRIDE
-    need = lib.fgq_quant_dispatch_workspace_bytes(4, 2, 3)
+    need = lib.fgq_quant_dispatch_workspace_bytes(4, 2, 3, 256)
     assert need > 0
     assert dispatch(lib, ws=0) == NULL
     assert dispatch(lib, ws_bytes=need - 1) == SHAPE
     assert dispatch(lib, ws=P + 65536 + 16) == ALIGN
-    assert lib.fgq_quant_dispatch_workspace_bytes(0, 8, 32) == 0
-    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32) == 2 * (4096 * 8 // 256) * 32 * 4   # 256-pair blocks
-    assert lib.fgq_quant_dispatch_workspace_bytes(-1, 8, 32) == 0
+    assert lib.fgq_quant_dispatch_workspace_bytes(0, 8, 32, 7168) == 0
+    # routing counts of 256-pair blocks (rounded to 256 bytes), then 4 bytes per token tile
+    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32, 0) == 2 * (4096 * 8 // 256) * 32 * 4
+    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32, 7168) == 2 * (4096 * 8 // 256) * 32 * 4 + 4096 * 56 * 4
+    assert lib.fgq_quant_dispatch_workspace_bytes(5, 1, 3, 128) == 256 + 5 * 4
+    assert lib.fgq_quant_dispatch_workspace_bytes(-1, 8, 32, 7168) == 0
+    assert lib.fgq_quant_dispatch_workspace_bytes(4096, 8, 32, 200) == 0
 
 
 # ---- power-of-two (E8M0) scale variants: byte scales, no alignment rule on them
