@@ -500,6 +500,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
 #pragma unroll
   for (int p = 0; p < C::NSTAGE - 1; ++p)
     if (kb_begin + p < kb_end) issue(kb_begin + p, p);
+  // tma = 0: the wave multiplies nothing but still issues its DMA share and
+  // meets every barrier (one per chunk, as in the other instantiations).
   auto kloop = [&](auto tma) {
     for (int kb = kb_begin; kb < kb_end; ++kb) {
       const int it = kb - kb_begin;
@@ -508,10 +510,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
       barrier_no_drain();
       if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-      eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
+      if constexpr (decltype(tma)::value > 0) eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
     }
   };
-  if constexpr (C::SKIP) {
+  // A wave whose rows all lie past the tile's last row (the short last slot
+  // of a grouped expert) runs the loop without arithmetic: its SIMD partner
+  // then has the matrix core and the vector ALU to itself.  Uniform per wave.
+  if (C::WAVES_M > 1 && (int64_t)eng.wm * C::WM >= row_end - row_begin) {
+    kloop(std::integral_constant<int, 0>{});
+  } else if constexpr (C::SKIP) {
     // sub-tile rows past the tile's last row hold no rows: skip them
     const int64_t rows = row_end - row_begin;
     if (rows <= C::BM / 4) kloop(std::integral_constant<int, C::TM / 4>{});
