@@ -557,7 +557,8 @@ using SplitCfg = TileCfg<64, 128, 1, 4, 3>;  // split-K, memory-bound small M: 3
 // dominate the traffic.  64 x 128 tiles with full-height waves: a slot runs
 // only the 16-row sub-tiles that hold rows, and two stages (49 KB of LDS)
 // leave room for three workgroups per CU; the slots of one expert share each
-// weight column block in L2 (tile_of keeps them together).
+// weight column block in L2 (the grouped kernel orders this configuration's
+// tiles by column block per XCD, slot fastest).
 using MoeDecodeCfg = TileCfg<64, 128, 1, 4, 2, true>;
 
 // ---------------------------------------------------------------------------
@@ -981,7 +982,19 @@ __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
   const int G = real_slots * tiles_n;
   if ((int)blockIdx.x >= G) return;  // no tile for this workgroup: the whole workgroup leaves
   int slot, tn;
-  tile_of(blockIdx.x, G, real_slots, slot, tn);
+  if constexpr (C::SKIP) {
+    // decode-shaped experts, weight-bound: each XCD owns a range of weight
+    // column blocks over all slots, slot fastest, so every (expert, column
+    // block) is fetched by one XCD and an expert's slots share it in L2
+    // (with m-tile groups an expert's slots could straddle two XCDs)
+    const int q = G / kXcds, r = G % kXcds;
+    const int xcd = (int)blockIdx.x % kXcds, local = (int)blockIdx.x / kXcds;
+    const int logical = xcd * q + (xcd < r ? xcd : r) + local;
+    tn = logical / real_slots;
+    slot = logical - tn * real_slots;
+  } else {
+    tile_of(blockIdx.x, G, real_slots, slot, tn);
+  }
   int e = -1;
   int64_t row_begin = 0, row_end = 0;
   int carried = 0;  // slots of the experts before e0 + j
