@@ -190,6 +190,14 @@ struct Engine16 {
   // weight scale at chunk 0, and the per-chunk strides; the byte sits at
   // (address mod 4) inside its DMA slot.
   uint32_t sa_lo = 0, sa_step = 0, sw_lo = 0, sw_step = 0;
+  // Promoting modes: the chunk sums of a chunk's last sub-tile row and their
+  // scales wait here and are added at the start of the next chunk (after its
+  // fragment loads are issued, so the wait on the matrix core overlaps LDS
+  // latency instead of stalling every wave just before the barrier), or by
+  // flush() after the last chunk.  Each accumulator still takes its chunk
+  // terms in chunk order.
+  v4f carry_t[C::TN];
+  v4f carry_s;
 
   __device__ __forceinline__ Engine16(int wave, int lane) {
     wm = wave / C::WAVES_N;
@@ -200,6 +208,9 @@ struct Engine16 {
     for (int mi = 0; mi < C::TM; ++mi)
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) acc[mi][ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    carry_s = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     // LDS byte offsets of this lane's fragment rows: logical columns 2 lgrp
     // and 2 lgrp + 1 of the 128-byte chunk row.  Sub-tile rows step by 16,
     // which keeps row & 15, so sub-tiles are base + 2048 * i; wave tile
@@ -211,6 +222,19 @@ struct Engine16 {
     b_off1 = C::A_BYTES + (wn * C::WN + l16) * 128 + (lds_col(c0 + 1, l16) << 4);
     sa_off = MODE >= 2 ? C::SA_OFF + (wm * C::WM + l16) * 4 : C::SA_OFF + (wm * C::WM + lgrp * 4) * 4;
     sw_idx = (wn * C::WN) / 128;
+  }
+
+  // adds the carried row (the last chunk's last sub-tile row); call once
+  // after the last chunk, with the TMA the chunks used
+  template <int TMA = C::TM>
+  __device__ __forceinline__ void flush() {
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) add4(acc[TMA - 1][ni], carry_t[ni]);
+    } else if constexpr (MODE != 3) {
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], carry_t[ni], carry_s);
+    }
   }
 
   // TMA: sub-tile rows that hold rows of the tile (the rest are skipped)
@@ -236,6 +260,10 @@ struct Engine16 {
     uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
     uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
     int sav = base[a_byte];
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) add4(acc[TMA - 1][ni], carry_t[ni]);  // the previous chunk's last row
+    }
     // promote: the chunk sums of sub-tile row mi are added one row later,
     // after the next row's operations are issued, so no add waits on the
     // operation that produces its input
@@ -274,7 +302,7 @@ struct Engine16 {
     }
     if constexpr (MODE == 2) {
 #pragma unroll
-      for (int ni = 0; ni < C::TN; ++ni) add4(acc[TMA - 1][ni], tp[ni]);
+      for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
     }
   }
 
@@ -312,6 +340,8 @@ struct Engine16 {
       uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
       uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
       v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], carry_t[ni], carry_s);  // the previous chunk's last row
       v4f tp[C::TN];
       v4f sp;
 #pragma unroll
@@ -341,7 +371,8 @@ struct Engine16 {
         sa4 = nsa;
       }
 #pragma unroll
-      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], tp[ni], sp);
+      for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
+      carry_s = sp;
     } else {
       // exact products: codes -> FP16 in registers, four K = 32 steps per chunk
       v8h bh[C::TN][4];
@@ -357,6 +388,8 @@ struct Engine16 {
       uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
       uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
       v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], carry_t[ni], carry_s);  // the previous chunk's last row
 #pragma unroll
       for (int mi = 0; mi < TMA; ++mi) {
         uint4 nlo = alo, nhi = ahi;
@@ -377,13 +410,14 @@ struct Engine16 {
           for (int ni = 0; ni < C::TN; ++ni)
             t[ni] = mfma_16x16x32_f16(a, bh[ni][ks], ks == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : t[ni]);
         }
-        const float s0 = sa4[0] * swv, s1 = sa4[1] * swv, s2 = sa4[2] * swv, s3 = sa4[3] * swv;
+        const v4f sc = {sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv};
+        if (mi + 1 < TMA) {
 #pragma unroll
-        for (int ni = 0; ni < C::TN; ++ni) {
-          acc[mi][ni][0] = __builtin_fmaf(t[ni][0], s0, acc[mi][ni][0]);
-          acc[mi][ni][1] = __builtin_fmaf(t[ni][1], s1, acc[mi][ni][1]);
-          acc[mi][ni][2] = __builtin_fmaf(t[ni][2], s2, acc[mi][ni][2]);
-          acc[mi][ni][3] = __builtin_fmaf(t[ni][3], s3, acc[mi][ni][3]);
+          for (int ni = 0; ni < C::TN; ++ni) fma4(acc[mi][ni], t[ni], sc);
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = t[ni];
+          carry_s = sc;
         }
         alo = nlo;
         ahi = nhi;
@@ -512,6 +546,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
       if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
       if constexpr (decltype(tma)::value > 0) eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
     }
+    if constexpr (decltype(tma)::value > 0) eng.template flush<decltype(tma)::value>();
   };
   // A wave whose rows all lie past the tile's last row (the short last slot
   // of a grouped expert) runs the loop without arithmetic: its SIMD partner
@@ -697,6 +732,7 @@ __device__ __forceinline__ void gemm_tile_fused(const uint16_t* __restrict__ a, 
     step(std::integral_constant<int, 0>{}, kb);
     if (kb + 1 < kb_end) step(std::integral_constant<int, 1>{}, kb + 1);
   }
+  eng.flush();
   eng.template store<PARTIAL>(row_begin, row_end, n0, c, part, ldc);
 }
 
