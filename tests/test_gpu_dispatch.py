@@ -70,6 +70,40 @@ def test_dispatch_routed_rows(fgq_gpu, T, topk, E, K, drop, seed):
     assert np.all(res["q"][R:] == CANARY)
 
 
+@pytest.mark.parametrize("e8m0", [False, True])
+@pytest.mark.parametrize("layout", ["row", "kmajor"])
+def test_dispatch_scale_layouts(fgq_gpu, layout, e8m0):
+    """Both ways the scales are written: contiguous per row (each routed row
+    gets its scales from the quantiser) and K-block-major (one scale per
+    token tile in the workspace, then a gather in row order).  Scales match
+    the oracle bit for bit; rows past the routed count and the guard bands
+    are never written."""
+    import torch
+    T, topk, E, K = 777, 4, 5, 640
+    R = T * topk
+    x = normal_bf16((T, K), 1.0, rng_for(11, 60))
+    ids = route_ids(T, topk, E, 1.1, rng_for(11, 61), drop=0.1)
+    dt = torch.uint8 if e8m0 else torch.float32
+    if layout == "row":
+        sg = Guarded(R, K // 128, dt)
+        s = sg.view
+    else:
+        sg = Guarded(K // 128, R, dt)
+        s = sg.view.t()
+    fn = fgq_gpu.quant_dispatch_1x128_e8m0 if e8m0 else fgq_gpu.quant_dispatch_1x128
+    q, s_out, off, src, dest = fn(dev_bf16(x), torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda(), E, s=s)
+    torch.cuda.synchronize()
+    sg.check_canaries()
+    ref = oracle.quant_dispatch_e8m0_ref if e8m0 else oracle.quant_dispatch_ref
+    qo, so, offo, _, _ = ref(x, ids, E)
+    Rr = int(offo[-1])
+    log(f"dispatch scales {layout} {'e8m0' if e8m0 else 'f32'}: {Rr} routed rows of {R}")
+    sh = np.ascontiguousarray(s.cpu().numpy())
+    assert np.array_equal(q.cpu().numpy()[:Rr], qo)
+    assert np.array_equal(sh[:Rr].view(np.uint8), np.ascontiguousarray(so).view(np.uint8))
+    assert np.all(sh[Rr:].view(np.uint8) == CANARY)
+
+
 def test_dispatch_out_of_range_ids(fgq_gpu):
     rng = np.random.default_rng(7)
     T, topk, E, K = 500, 3, 9, 256
