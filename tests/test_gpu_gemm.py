@@ -332,3 +332,36 @@ def test_grouped_moe_decode_full_size(fgq_gpu, mode):
         qwo, swo = oracle.quant_w_128x128(W[e])
         ref = oracle.gemm_ref(qao, sao, qwo, swo)
         _check(host_bf16_f64(c[r0:r1]), ref, f"moe_decode expert {e} ({r1 - r0} rows)", mode, qao, sao, qwo, swo)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_gemm_and_grouped_deterministic(fgq_gpu, mode):
+    """Repeated calls on the same inputs give byte-identical C on the
+    large-tile path, the split-K path (a decode shape) and the grouped path,
+    with other launches in between: nothing depends on timing (no atomics,
+    fixed reduction orders)."""
+    import torch
+    E = 4
+    a = dev_bf16(normal_bf16((640, 2048), 1.0, rng_for(40, 1)))
+    ad = dev_bf16(normal_bf16((64, 7168), 1.0, rng_for(40, 2)))
+    w = dev_bf16(normal_bf16((1024, 2048), 0.02, rng_for(40, 3)))
+    wd = dev_bf16(normal_bf16((4096, 7168), 0.02, rng_for(40, 4)))
+    wg = dev_bf16(normal_bf16((E, 256, 2048), 0.02, rng_for(40, 5)))
+    qa, sa = fgq_gpu.quant_act_1x128(a)
+    qad, sad = fgq_gpu.quant_act_1x128(ad)
+    qw, sw = fgq_gpu.quant_w_128x128(w)
+    qwd, swd = fgq_gpu.quant_w_128x128(wd)
+    qwg, swg = fgq_gpu.quant_w_128x128(wg)
+    off = torch.tensor([0, 300, 300, 557, 640], dtype=torch.int32, device="cuda")
+    runs = {
+        "dense": lambda: fgq_gpu.gemm_fp8_blockscaled(qa, sa, qw, sw, mode=mode),
+        "split-K": lambda: fgq_gpu.gemm_fp8_blockscaled(qad, sad, qwd, swd, mode=mode),
+        "grouped": lambda: fgq_gpu.grouped_gemm_fp8_blockscaled(qa, sa, qwg, swg, off, mode=mode),
+    }
+    first = {k: f().clone() for k, f in runs.items()}
+    for rep in range(4):
+        for k, f in runs.items():
+            c = f()
+            torch.cuda.synchronize()
+            assert torch.equal(c.view(torch.int16), first[k].view(torch.int16)), (k, rep)
+    log(f"GEMM determinism mode {mode}: 5 runs each of dense, split-K and grouped identical")
