@@ -972,10 +972,11 @@ hipError_t launch_gemm_bf16a_fp8_blockscaled(const uint16_t* a, int64_t lda, con
 // ---------------------------------------------------------------------------
 // Grouped (MoE) variant.  The linear workgroup id maps (as above) to an
 // (m-tile slot, n-tile) pair; slots run over all experts in expert order.
-// The slot -> (expert, rows) map is computed on the GPU from offsets[] with
-// a workgroup-wide prefix sum over the per-expert tile counts, so the host
-// never reads the routing result.  The grid is sized for the most slots the
-// sizes allow; workgroups beyond the real tiles leave at once.
+// The slot -> (expert, rows) map is computed on the GPU from offsets[] (a
+// running sum of the per-expert slot counts, done by every wave), so the
+// host never reads the routing result.  The grid is sized for the most
+// slots the sizes allow; workgroup ids are dealt over the real tiles and
+// the rest leave at once.
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT) void k_grouped_gemm_fp8_bs(
     const uint8_t* __restrict__ qa, int64_t lda, const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
