@@ -92,7 +92,7 @@ fgq_status_t check_gemm(const void* qa, int64_t lda, const void* sa, int64_t sa_
                                       s_align);
   if (st != FGQ_OK) return st;
   if (M >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
-  const size_t need = fgq::gemm_workspace_bytes(M, N, K);
+  const size_t need = fgq::gemm_workspace_required(M, N, K);
   if (need > 0) {
     if (!workspace) return FGQ_ERR_NULL;
     if (workspace_bytes < need) return FGQ_ERR_SHAPE;
@@ -209,7 +209,7 @@ fgq_status_t fgq_gemm_bf16a_fp8_blockscaled(const void* a, int64_t lda, const vo
     if (!aligned(qa_out, 16) || !aligned(sa_out, 4)) return FGQ_ERR_ALIGN;
     if (ldq < K || ldq % 16 != 0 || sa_sm < 0 || sa_skb < 0) return FGQ_ERR_STRIDE;
   }
-  const size_t need = fgq::gemm_workspace_bytes(M, N, K);
+  const size_t need = fgq::gemm_workspace_required(M, N, K);
   if (need > 0) {
     if (!workspace) return FGQ_ERR_NULL;
     if (workspace_bytes < need) return FGQ_ERR_SHAPE;

@@ -25,7 +25,10 @@ hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const flo
                                        int64_t M, int64_t N, int64_t K, int mode, void* workspace,
                                        size_t workspace_bytes, hipStream_t st);
 
+// recommended size (lets large products split their last round) and the
+// size the call requires (split-K of small M)
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t gemm_workspace_required(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_grouped_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa,
                                                int64_t sa_sm, int64_t sa_skb, const uint8_t* qw,

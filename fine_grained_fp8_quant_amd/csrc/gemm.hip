@@ -427,7 +427,9 @@ struct Engine16 {
   }
 
   // lane holds rows lgrp*4 + i, column l16 of each 16x16 sub-tile
-  template <bool PARTIAL>
+  // PARTIAL 0: BF16 C; 1: binary32 sums to part[m * ldc + n]; 2: binary32
+  // sums to the tile's own block, part[(m - row_begin) * BN + n - n0]
+  template <int PARTIAL>
   __device__ __forceinline__ void store(int64_t row_begin, int64_t row_end, int64_t n0, uint16_t* __restrict__ c,
                                         float* __restrict__ part, int64_t ldc) {
 #pragma unroll
@@ -436,7 +438,11 @@ struct Engine16 {
       for (int i = 0; i < 4; ++i) {
         const int64_t gr = row_begin + wm * C::WM + mi * 16 + lgrp * 4 + i;
         if (gr < row_end) {
-          if constexpr (PARTIAL) {
+          if constexpr (PARTIAL == 2) {
+            float* prow = part + (gr - row_begin) * C::BN + wn * C::WN + l16;
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni) prow[ni * 16] = acc[mi][ni][i];
+          } else if constexpr (PARTIAL == 1) {
             float* prow = part + gr * ldc + n0 + wn * C::WN + l16;
 #pragma unroll
             for (int ni = 0; ni < C::TN; ++ni) prow[ni * 16] = acc[mi][ni][i];
@@ -454,8 +460,9 @@ struct Engine16 {
 // One output tile [row_begin, row_begin + BM) x [n0, n0 + BN) over the K
 // chunks [kb_begin, kb_end); rows >= row_end are neither read (their loads
 // repeat row row_end - 1) nor written.  Writes BF16 C, or with PARTIAL the
-// binary32 sums of its chunks to part[m * ldc + n] (split-K workspace).
-template <class C, int MODE, bool PARTIAL = false>
+// binary32 sums of its chunks to part[m * ldc + n] (PARTIAL 1, split-K
+// workspace) or to the tile's own BM x BN block at part (PARTIAL 2).
+template <class C, int MODE, int PARTIAL = 0>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_t lda,
                                           const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm, int64_t sa_skb,
                                           int64_t row_begin, int64_t row_end,
@@ -776,10 +783,12 @@ __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs(const uint8_t* __restrict
                                                        int64_t ldw, const ScaleOf<MODE>* __restrict__ sw,
                                                        int64_t sw_snb, int64_t sw_skb,
                                                        uint16_t* __restrict__ c, int64_t ldc, int64_t M,
-                                                       int tiles_m, int KB) {
+                                                       int tiles_m, int KB, int G) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
+  // G: the tiles of the whole product; the grid may cover only the first
+  // ones (k_gemm_fp8_bs_tail takes the rest)
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+  tile_of(blockIdx.x, G, tiles_m, tm, tn);
   gemm_tile<C, MODE>(qa, lda, sa, sa_sm, sa_skb, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
                      (int64_t)tn * C::BN, c, nullptr, ldc, 0, KB, lds);
 }
@@ -799,7 +808,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs_splitk(const uint8_t* __r
   int tm, tn;
   tile_of(blockIdx.x % tiles, tiles, tiles_m, tm, tn);
   const int kb0 = (int)((int64_t)split * KB / S), kb1 = (int)((int64_t)(split + 1) * KB / S);
-  gemm_tile<C, MODE, true>(qa, lda, sa, sa_sm, sa_skb, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
+  gemm_tile<C, MODE, 1>(qa, lda, sa, sa_sm, sa_skb, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
                            (int64_t)tn * C::BN, nullptr, part + (int64_t)split * M * N, N, kb0, kb1, lds);
 }
 
@@ -828,6 +837,61 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   *reinterpret_cast<uint4*>(c + m * ldc + n) = o;
 }
 
+// The last, partly filled round of a large dense product: its `rem` tiles
+// (the last ones of the tile order) are split S ways along K so that they
+// spread over the compute units the round would leave idle.  Workgroup i
+// takes tile t = i mod rem and K part s = i / rem, and writes its binary32
+// sums to the tile's own BM x BN block part[s * rem + t].
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT) void k_gemm_fp8_bs_tail(const uint8_t* __restrict__ qa, int64_t lda,
+                                                            const ScaleOf<MODE>* __restrict__ sa, int64_t sa_sm,
+                                                            int64_t sa_skb, const uint8_t* __restrict__ qw,
+                                                            int64_t ldw, const ScaleOf<MODE>* __restrict__ sw,
+                                                            int64_t sw_snb, int64_t sw_skb,
+                                                            float* __restrict__ part, int64_t M, int tiles_m,
+                                                            int G, int rem, int KB, int S) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * C::STAGE];
+  const int t = (int)blockIdx.x % rem, split = (int)blockIdx.x / rem;
+  int tm, tn;
+  tile_of(G - rem + t, G, tiles_m, tm, tn);
+  const int kb0 = (int)((int64_t)split * KB / S), kb1 = (int)((int64_t)(split + 1) * KB / S);
+  gemm_tile<C, MODE, 2>(qa, lda, sa, sa_sm, sa_skb, (int64_t)tm * C::BM, M, qw, ldw, sw, sw_snb, sw_skb,
+                        (int64_t)tn * C::BN, nullptr, part + ((int64_t)split * rem + t) * C::BM * C::BN, C::BN,
+                        kb0, kb1, lds);
+}
+
+// C of the tail tiles: the sum of their S partial blocks in split order
+// (deterministic), eight consecutive outputs per thread; tile t = blockIdx.y.
+template <class C>
+__global__ __launch_bounds__(256) void k_tail_reduce(const float* __restrict__ part, int S, int rem, int G,
+                                                     int tiles_m, int64_t M, uint16_t* __restrict__ c, int64_t ldc) {
+  const int t = (int)blockIdx.y;
+  const int e = ((int)blockIdx.x * 256 + (int)threadIdx.x) * 8;
+  if (e >= C::BM * C::BN) return;
+  int tm, tn;
+  tile_of(G - rem + t, G, tiles_m, tm, tn);
+  const int r = e / C::BN, col = e - r * C::BN;
+  const int64_t row = (int64_t)tm * C::BM + r;
+  if (row >= M) return;
+  float v[8];
+  const int64_t blk = (int64_t)C::BM * C::BN;
+  const float4* p = reinterpret_cast<const float4*>(part + (int64_t)t * blk + e);
+  float4 x = p[0], y = p[1];
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  for (int sp = 1; sp < S; ++sp) {
+    p = reinterpret_cast<const float4*>(part + ((int64_t)sp * rem + t) * blk + e);
+    x = p[0];
+    y = p[1];
+    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w; v[4] += y.x; v[5] += y.y; v[6] += y.z; v[7] += y.w;
+  }
+  uint4 o;
+  o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+  o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+  o.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+  o.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  *reinterpret_cast<uint4*>(c + row * ldc + (int64_t)tn * C::BN + col) = o;
+}
+
 // Split-K plan for a dense shape: S > 1 when M is small enough that the
 // output tiles alone cannot fill the 256 compute units several times over.
 // The same function decides the workspace size and the launch.
@@ -851,9 +915,49 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+// Large dense products run one workgroup per compute unit (gfx950 has
+// 256), so a product of G tiles takes G / 256 rounds.  When the last round
+// holds at most half the units' worth of tiles, those rem tiles are split
+// S ways along K (k_gemm_fp8_bs_tail, k_tail_reduce) if the caller's
+// workspace holds their partial blocks; otherwise the plain launch runs.
+constexpr int kComputeUnits = 256;
+struct TailPlan {
+  int S = 1;
+  int G = 0, rem = 0, tiles_m = 0;
+};
+template <class C>
+static TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
+  static_assert(C::NSTAGE * C::STAGE > 80 * 1024, "one workgroup per compute unit");
+  TailPlan p;
+  if (M <= 128 || N % C::BN != 0) return p;
+  p.tiles_m = (int)((M + C::BM - 1) / C::BM);
+  p.G = p.tiles_m * (int)(N / C::BN);
+  p.rem = p.G % kComputeUnits;
+  const int KB = (int)(K / 128);
+  if (p.G < kComputeUnits || p.rem == 0 || p.rem > kComputeUnits / 2) return p;
+  int S = kComputeUnits / p.rem;
+  if (S > KB / 4) S = KB / 4;  // at least 4 chunks per part
+  if (S > 16) S = 16;
+  p.S = S < 2 ? 1 : S;
+  return p;
+}
+template <class C>
+static size_t tail_bytes(const TailPlan& p) {
+  return p.S > 1 ? (size_t)p.S * (size_t)p.rem * C::BM * C::BN * sizeof(float) : 0;
+}
+
+size_t gemm_workspace_required(int64_t M, int64_t N, int64_t K) {
   const SplitPlan p = split_plan(M, N, K);
   return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  size_t b = gemm_workspace_required(M, N, K);
+  const size_t t0 = tail_bytes<BigExactCfg>(tail_plan<BigExactCfg>(M, N, K));
+  const size_t t1 = tail_bytes<BigCfg>(tail_plan<BigCfg>(M, N, K));
+  if (t0 > b) b = t0;
+  if (t1 > b) b = t1;
+  return b;
 }
 
 template <class C, int MODE>
@@ -863,7 +967,21 @@ static void launch_dense(const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa
   const int tiles_m = (int)((M + C::BM - 1) / C::BM);
   const int tiles_n = (int)(N / C::BN);
   hipLaunchKernelGGL((k_gemm_fp8_bs<C, MODE>), dim3(tiles_m * tiles_n), dim3(C::NT), 0, st, qa, lda, sa, sa_sm,
-                     sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, tiles_m, (int)(K / 128));
+                     sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, tiles_m, (int)(K / 128), tiles_m * tiles_n);
+}
+
+template <class C, int MODE>
+static void launch_dense_tail(const TailPlan& p, const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa,
+                              int64_t sa_sm, int64_t sa_skb, const uint8_t* qw, int64_t ldw, const ScaleOf<MODE>* sw,
+                              int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc, int64_t M, int64_t K,
+                              float* part, hipStream_t st) {
+  const int KB = (int)(K / 128);
+  hipLaunchKernelGGL((k_gemm_fp8_bs<C, MODE>), dim3(p.G - p.rem), dim3(C::NT), 0, st, qa, lda, sa, sa_sm, sa_skb,
+                     qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, p.tiles_m, KB, p.G);
+  hipLaunchKernelGGL((k_gemm_fp8_bs_tail<C, MODE>), dim3(p.rem * p.S), dim3(C::NT), 0, st, qa, lda, sa, sa_sm,
+                     sa_skb, qw, ldw, sw, sw_snb, sw_skb, part, M, p.tiles_m, p.G, p.rem, KB, p.S);
+  hipLaunchKernelGGL((k_tail_reduce<C>), dim3((C::BM * C::BN / 8 + 255) / 256, p.rem), dim3(256), 0, st, part, p.S,
+                     p.rem, p.G, p.tiles_m, M, c, ldc);
 }
 
 template <int MODE>
@@ -888,33 +1006,48 @@ template <int MODE>
 static hipError_t gemm_dispatch(const uint8_t* qa, int64_t lda, const ScaleOf<MODE>* sa, int64_t sa_sm,
                                 int64_t sa_skb, const uint8_t* qw, int64_t ldw, const ScaleOf<MODE>* sw,
                                 int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
-                                int64_t K, void* workspace, hipStream_t st) {
+                                int64_t K, void* workspace, size_t workspace_bytes, hipStream_t st) {
   const SplitPlan p = split_plan(M, N, K);
   float* part = static_cast<float*>(workspace);
   const bool big = M > 128 && N % 256 == 0;
-  if (p.S > 1) launch_splitk<MODE>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
-  else if (big) launch_dense<BigOf<MODE>, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
-  else launch_dense<SmallCfg, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+  if (p.S > 1) {
+    launch_splitk<MODE>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
+  } else if (big) {
+    using C = BigOf<MODE>;
+    const TailPlan tp = tail_plan<C>(M, N, K);
+    const bool room = workspace && (reinterpret_cast<uintptr_t>(workspace) & 15) == 0 &&
+                      workspace_bytes >= tail_bytes<C>(tp);
+    if (tp.S > 1 && room)
+      launch_dense_tail<C, MODE>(tp, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, K, part, st);
+    else
+      launch_dense<C, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+  } else {
+    launch_dense<SmallCfg, MODE>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                        int64_t sa_skb, const uint8_t* qw, int64_t ldw, const float* sw,
                                        int64_t sw_snb, int64_t sw_skb, uint16_t* c, int64_t ldc,
-                                       int64_t M, int64_t N, int64_t K, int mode, void* workspace, size_t,
-                                       hipStream_t st) {
+                                       int64_t M, int64_t N, int64_t K, int mode, void* workspace,
+                                       size_t workspace_bytes, hipStream_t st) {
   if (mode == 1)
-    return gemm_dispatch<1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
-  return gemm_dispatch<0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
+    return gemm_dispatch<1>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace,
+                            workspace_bytes, st);
+  return gemm_dispatch<0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace,
+                            workspace_bytes, st);
 }
 
 hipError_t launch_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm, int64_t sa_skb,
                                 const uint8_t* qw, int64_t ldw, const uint8_t* sw, int64_t sw_snb, int64_t sw_skb,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int in_core,
-                                void* workspace, size_t, hipStream_t st) {
+                                void* workspace, size_t workspace_bytes, hipStream_t st) {
   if (in_core)
-    return gemm_dispatch<3>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
-  return gemm_dispatch<2>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace, st);
+    return gemm_dispatch<3>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace,
+                            workspace_bytes, st);
+  return gemm_dispatch<2>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace,
+                            workspace_bytes, st);
 }
 
 // BF16 activations quantised inside the GEMM (see gemm_tile_fused).  Same

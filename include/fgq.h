@@ -159,14 +159,20 @@ enum { FGQ_GEMM_EXACT = 0, FGQ_GEMM_FP8_CORE = 1 };
  *   sw     float, sw[nb * sw_snb + kb * sw_skb].
  *   c      BF16 [M, N] output, row stride ldc (>= N, multiple of 8); 16-byte aligned.
  *   mode   FGQ_GEMM_EXACT or FGQ_GEMM_FP8_CORE (anything else: FGQ_ERR_UNSUPPORTED).
- *   workspace / workspace_bytes: scratch the caller provides; at least
- *          fgq_gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned (may be
- *          NULL when that is 0).
+ *   workspace / workspace_bytes: scratch the caller provides, 256-byte
+ *          aligned; fgq_gemm_workspace_bytes(M, N, K) bytes is the size that
+ *          lets every shape take its fastest launch.  Small M (split along
+ *          K) requires that size; otherwise the call runs with any size,
+ *          NULL included: a large product whose last round of tiles would
+ *          leave most compute units idle splits those tiles along K when
+ *          the workspace holds their partial sums, and runs plainly when it
+ *          does not.
  *   N and K must be multiples of 128, K > 0.  M >= 0 (any value; M = 0
  *   launches nothing).
  * The result is within the tolerance of the float64 definition; the order of
  * the additions inside a chunk is the matrix core's, so results are
- * reproducible run to run but not across tile configurations.
+ * reproducible run to run (for the same workspace size) but not across tile
+ * configurations.
  */
 fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                       int64_t sa_skb, const void* qw, int64_t ldw, const float* sw,
@@ -174,7 +180,9 @@ fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* 
                                       int64_t M, int64_t N, int64_t K, int32_t mode, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace fgq_gemm_fp8_blockscaled needs for this shape (0 = none). */
+/* Bytes of workspace for fgq_gemm_fp8_blockscaled (and its E8M0 variant) at
+ * this shape: what small M requires, and what lets a large product split its
+ * last round (0 = none). */
 size_t fgq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*

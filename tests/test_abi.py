@@ -129,7 +129,12 @@ def test_gemm_validation(lib):
     # small M (memory-bound) shapes split K and need an FP32 workspace
     need = lib.fgq_gemm_workspace_bytes(64, 18432, 7168)
     assert need > 0 and need % (64 * 18432 * 4) == 0
-    assert lib.fgq_gemm_workspace_bytes(8192, 18432, 7168) == 0
+    # large M: partial sums for the last round's tiles, split along K.  8192 rows in
+    # 192x256 tiles (exact mode) are 3096 tiles: 12 rounds of 256 and 24 tiles,
+    # split 10 ways (the FP8 tiles, 2304 of them, fill 9 rounds exactly)
+    assert lib.fgq_gemm_workspace_bytes(8192, 18432, 7168) == 24 * 10 * 192 * 256 * 4
+    # a last round more than half full is not split
+    assert lib.fgq_gemm_workspace_bytes(8064, 18432, 7168) == 0
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL     # no workspace
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P + 16, ws_bytes=need) == ALIGN

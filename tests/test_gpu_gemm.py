@@ -365,3 +365,26 @@ def test_gemm_and_grouped_deterministic(fgq_gpu, mode):
             torch.cuda.synchronize()
             assert torch.equal(c.view(torch.int16), first[k].view(torch.int16)), (k, rep)
     log(f"GEMM determinism mode {mode}: 5 runs each of dense, split-K and grouped identical")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K", [(2112, 6144, 1024), (2816, 6144, 2048)])
+def test_gemm_last_round_split(fgq_gpu, M, N, K, mode):
+    """Large products whose last round of tiles is split along K into
+    partial sums in the workspace (2112 rows: the exact mode's 264 tiles are
+    one round and 8; 2816 rows: both modes, up to 4 parts): the tolerance
+    gate with the workspace, and without one (the plain launch)."""
+    import torch
+    a = normal_bf16((M, K), 1.0, rng_for(41, M))
+    w = normal_bf16((N, K), 0.02, rng_for(41, N))
+    qa, sa = oracle.quant_act_1x128(a)
+    qw, sw = oracle.quant_w_128x128(w)
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    assert fgq_gpu.gemm_workspace_bytes(M, N, K) > 0
+    qa_d, sa_d, qw_d, sw_d = dev_u8(qa), dev_f32(sa), dev_u8(qw), dev_f32(sw)
+    c_split = fgq_gpu.gemm_fp8_blockscaled(qa_d, sa_d, qw_d, sw_d, mode=mode)
+    c_plain = fgq_gpu.gemm_fp8_blockscaled(qa_d, sa_d, qw_d, sw_d, mode=mode,
+                                           workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    _check(host_bf16_f64(c_split), ref, f"last-round split {M}x{N}x{K}", mode, qa, sa, qw, sw)
+    _check(host_bf16_f64(c_plain), ref, f"plain {M}x{N}x{K}", mode, qa, sa, qw, sw)
