@@ -69,6 +69,12 @@ def api_of(kname: str, e8: bool):
         return "gemm_bf16a_fp8_blockscaled", mode
     if kname.startswith("k_grouped"):
         return ("grouped_gemm_fp8_e8m0" if e8 else "grouped_gemm_fp8_blockscaled"), mode
+    if kname.startswith("k_tail_reduce"):
+        # the last-round reduction of the dense GEMM: 192-row tiles are the exact mode's
+        api = "gemm_fp8_e8m0" if e8 else "gemm_fp8_blockscaled"
+        if "<192," in kname:
+            return api, "exact"
+        return api, (None if e8 else "fp8core")
     if kname.startswith("k_gemm") or kname.startswith("k_splitk"):
         return ("gemm_fp8_e8m0" if e8 else "gemm_fp8_blockscaled"), mode
     return None, None
@@ -120,6 +126,21 @@ def summarise(out_dir, spec, traffic):
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
         lines.append(f"| {name} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f} |")
+    # one call of the C ABI can launch several kernels (split-K and its
+    # reduction; the dense last-round split and its reduction): their
+    # average durations add up to the call
+    per_call = defaultdict(float)
+    for name, calls, avg, mn, mx, pct in stats:
+        api, mode = api_of(name, e8)
+        if not api:
+            continue
+        modes = [mode] if mode or "gemm" not in api else (["promote", "incore"] if e8 else ["exact", "fp8core"])
+        for md in modes:
+            per_call[api + (f"[{md}]" if md else "")] += avg
+    lines += ["", "Per call (sum of the average durations of the call's kernels):", "",
+              "| call | avg us |", "|---|---|"]
+    for key in sorted(per_call):
+        lines.append(f"| {key} | {per_call[key]:.1f} |")
     lines += ["", "## HBM traffic per launch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
               f"Calibration from the 1 GiB copy in the same runs: FETCH_SIZE x{f_factor:.3f}, "
               f"WRITE_SIZE x{w_factor:.3f}.", "",
