@@ -198,6 +198,16 @@ struct Engine16 {
   // terms in chunk order.
   v4f carry_t[C::TN];
   v4f carry_s;
+  // Exact mode on full-height tiles: the chunk's last sub-tile row is
+  // multiplied at the start of the next chunk (or by flush()), after the
+  // barrier, so its matrix-core work covers the latency of the next chunk's
+  // fragment loads.  Its operands wait in registers: the chunk's B fragments
+  // (FP16), the row's A codes and its promotion scales.  Every accumulator
+  // still takes its chunk terms in chunk order.
+  static constexpr bool DEFER = MODE == 0 && !C::SKIP;
+  v8h bhm[C::TN][4];
+  uint4 pa_lo, pa_hi;
+  v4f psc;
 
   __device__ __forceinline__ Engine16(int wave, int lane) {
     wm = wave / C::WAVES_N;
@@ -211,6 +221,13 @@ struct Engine16 {
 #pragma unroll
     for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     carry_s = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    // the first chunk's deferred row multiplies zeros into zero sums
+#pragma unroll
+    for (int ni = 0; ni < C::TN; ++ni)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bhm[ni][ks] = (v8h){};
+    pa_lo = pa_hi = (uint4){0u, 0u, 0u, 0u};
+    psc = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     // LDS byte offsets of this lane's fragment rows: logical columns 2 lgrp
     // and 2 lgrp + 1 of the 128-byte chunk row.  Sub-tile rows step by 16,
     // which keeps row & 15, so sub-tiles are base + 2048 * i; wave tile
@@ -228,7 +245,9 @@ struct Engine16 {
   // after the last chunk, with the TMA the chunks used
   template <int TMA = C::TM>
   __device__ __forceinline__ void flush() {
-    if constexpr (MODE == 2) {
+    if constexpr (DEFER) {
+      exact_row(acc[TMA - 1], pa_lo, pa_hi, psc);
+    } else if constexpr (MODE == 2) {
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) add4(acc[TMA - 1][ni], carry_t[ni]);
     } else if constexpr (MODE != 3) {
@@ -322,6 +341,22 @@ struct Engine16 {
     a[3] += t[3];
   }
 
+  // one sub-tile row, exact products: four K = 32 steps against the B
+  // fragments in bhm, then the promotion a += t * sc
+  __device__ __forceinline__ void exact_row(v4f (&arow)[C::TN], const uint4& lo, const uint4& hi, const v4f& sc) {
+    const uint32_t aw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    v4f t[C::TN];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v8h a = e4m3x8_to_f16(aw[2 * ks], aw[2 * ks + 1]);
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni)
+        t[ni] = mfma_16x16x32_f16(a, bhm[ni][ks], ks == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : t[ni]);
+    }
+#pragma unroll
+    for (int ni = 0; ni < C::TN; ++ni) fma4(arow[ni], t[ni], sc);
+  }
+
   // binary32 scales: the chunk's FP32 sum, then promotion by the vector ALU
   template <int TMA>
   __device__ __forceinline__ void chunk_f32(const uint8_t* base) {
@@ -373,6 +408,49 @@ struct Engine16 {
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
       carry_s = sp;
+    } else if constexpr (DEFER) {
+      // exact products, last row deferred.  Half the B fragments are
+      // requested before the previous chunk's last row runs, the rest after
+      // it has taken their registers' old values.
+      constexpr int H = C::TN / 2;
+      uint4 blo[H], bhi[H];
+#pragma unroll
+      for (int ni = 0; ni < H; ++ni) {
+        blo[ni] = *reinterpret_cast<const uint4*>(base + b_off0 + ni * 2048);
+        bhi[ni] = *reinterpret_cast<const uint4*>(base + b_off1 + ni * 2048);
+      }
+      uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
+      uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
+      v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
+      exact_row(acc[TMA - 1], pa_lo, pa_hi, psc);  // the previous chunk's last row
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) {
+        uint4 lo, hi;
+        if (ni < H) {
+          lo = blo[ni < H ? ni : 0];
+          hi = bhi[ni < H ? ni : 0];
+        } else {
+          lo = *reinterpret_cast<const uint4*>(base + b_off0 + ni * 2048);
+          hi = *reinterpret_cast<const uint4*>(base + b_off1 + ni * 2048);
+        }
+        bhm[ni][0] = e4m3x8_to_f16(lo.x, lo.y);
+        bhm[ni][1] = e4m3x8_to_f16(lo.z, lo.w);
+        bhm[ni][2] = e4m3x8_to_f16(hi.x, hi.y);
+        bhm[ni][3] = e4m3x8_to_f16(hi.z, hi.w);
+      }
+#pragma unroll
+      for (int mi = 0; mi + 1 < TMA; ++mi) {
+        const uint4 nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+        const uint4 nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+        const v4f nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
+        exact_row(acc[mi], alo, ahi, (v4f){sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv});
+        alo = nlo;
+        ahi = nhi;
+        sa4 = nsa;
+      }
+      pa_lo = alo;
+      pa_hi = ahi;
+      psc = (v4f){sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv};
     } else {
       // exact products: codes -> FP16 in registers, four K = 32 steps per chunk
       v8h bh[C::TN][4];
