@@ -379,6 +379,35 @@ def test_gemm8_workloads(fgq_gpu, name, rows, acc):
 
 
 @pytest.mark.parametrize("acc", ACCS)
+def test_gemm8_last_round_split(fgq_gpu, acc):
+    """2816 rows in 256x256 tiles are one round of 256 tiles and 8 more: the
+    last 8 are split 4 ways along K into partial sums in the workspace.  The
+    split and the plain launch (no workspace) against the oracle; promote
+    also bit for bit against the FP8-core mode fed the same power-of-two
+    scales as binary32, which takes the same split."""
+    import torch
+    M, N, K = 2816, 6144, 2048
+    a = normal_bf16((M, K), 1.0, rng_for(42, M))
+    w = normal_bf16((N, K), 0.02, rng_for(42, N))
+    qa, ba = oracle.quant_act_1x128_e8m0(a)
+    qw, bw = oracle.quant_w_128x128_e8m0(w)
+    ref = oracle.gemm_e8m0_ref(qa, ba, qw, bw)
+    assert fgq_gpu.gemm_workspace_bytes(M, N, K) > 0
+    qa_d, ba_d, qw_d, bw_d = dev_u8(qa), dev_u8(ba), dev_u8(qw), dev_u8(bw)
+    c_split = fgq_gpu.gemm_fp8_e8m0(qa_d, ba_d, qw_d, bw_d, accumulate=acc)
+    c_plain = fgq_gpu.gemm_fp8_e8m0(qa_d, ba_d, qw_d, bw_d, accumulate=acc,
+                                    workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    split, plain = host_bf16_f64(c_split), host_bf16_f64(c_plain)
+    _check8(split, ref, f"e8m0 last-round split {M}x{N}x{K}", acc, qa, ba, qw, bw)
+    _check8(plain, ref, f"e8m0 plain {M}x{N}x{K}", acc, qa, ba, qw, bw)
+    if acc == PROMOTE:
+        cf = _gemm_f32(fgq_gpu, qa, oracle.e8m0_decode(ba).astype(np.float32), qw,
+                       oracle.e8m0_decode(bw).astype(np.float32), 1)
+        assert np.array_equal(split, cf)
+
+
+@pytest.mark.parametrize("acc", ACCS)
 def test_gemm8_prefill_full_size_sampled(fgq_gpu, acc):
     """8192 x 18432 x 7168 quantised and multiplied on the GPU as the
     benchmark runs it; 128 sampled rows against the oracle."""
