@@ -191,7 +191,8 @@ struct Engine16 {
   // weight scale at chunk 0, and the per-chunk strides; the byte sits at
   // (address mod 4) inside its DMA slot.
   uint32_t sa_lo = 0, sa_step = 0, sw_lo = 0, sw_step = 0;
-  // Promoting modes: the chunk sums of a chunk's last sub-tile row and their
+  // Promoting modes (FP8 core, E8M0 promote, and the exact mode on
+  // row-skipping tiles): the chunk sums of a chunk's last sub-tile row and their
   // scales wait here and are added at the start of the next chunk (after its
   // fragment loads are issued, so the wait on the matrix core overlaps LDS
   // latency instead of stalling every wave just before the barrier), or by
