@@ -45,6 +45,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "fine_grained_fp8_quant_amd", "csrc", "gemm.hip")
 QUANT_SOURCE = os.path.join(ROOT, "fine_grained_fp8_quant_amd", "csrc", "quant.hip")
+DISPATCH_SOURCE = os.path.join(ROOT, "fine_grained_fp8_quant_amd", "csrc", "dispatch.hip")
 
 WORKLOAD_TITLES = {
     "prefill": "dense prefill GEMM 8192x7168x18432 (A 1x128 + W 128x128 E4M3 quant + GEMM)",
@@ -366,7 +367,7 @@ def traffic_for(kernel):
     entry = t.get(kernel)
     if not entry:
         return None
-    src = GEMM_SOURCE if "gemm" in kernel else QUANT_SOURCE
+    src = GEMM_SOURCE if "gemm" in kernel else (DISPATCH_SOURCE if "dispatch" in kernel else QUANT_SOURCE)
     if entry.get("source_sha") != sha(src):
         return None
     return entry.get("bytes_per_launch")
