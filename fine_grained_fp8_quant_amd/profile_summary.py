@@ -70,11 +70,15 @@ def api_of(kname: str, e8: bool):
     if kname.startswith("k_grouped"):
         return ("grouped_gemm_fp8_e8m0" if e8 else "grouped_gemm_fp8_blockscaled"), mode
     if kname.startswith("k_tail_reduce"):
-        # the last-round reduction of the dense GEMM: 192-row tiles are the exact mode's
+        # the last-round reduction of the dense GEMM, named by its tile
+        # configuration: 192-row tiles are the exact mode's, sixteen waves
+        # (4 x 4) the in-core mode's
         api = "gemm_fp8_e8m0" if e8 else "gemm_fp8_blockscaled"
         if "<192," in kname:
             return api, "exact"
-        return api, (None if e8 else "fp8core")
+        if e8:
+            return api, ("incore" if re.search(r"<256, 256, 4, 4\b", kname) else "promote")
+        return api, "fp8core"
     if kname.startswith("k_gemm") or kname.startswith("k_splitk"):
         return ("gemm_fp8_e8m0" if e8 else "gemm_fp8_blockscaled"), mode
     return None, None
