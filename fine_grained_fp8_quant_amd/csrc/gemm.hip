@@ -674,13 +674,17 @@ __device__ __forceinline__ void tile_of(int bid, int G, int tiles_m, int& tm, in
 using BigCfg = TileCfg<256, 256, 2, 4>;      // FP8 matrix core, large M
 using BigExactCfg = TileCfg<192, 256, 2, 4>; // exact products, large M (FP16 operands need more registers)
 using SmallCfg = TileCfg<64, 128, 1, 4>;
-// Exact-mode grouped products with short K (at most 16 chunks): with one
-// workgroup per CU each tile's pipeline fill and C stores stand alone, and
-// the large tiles end on a partly filled round.  These 67 KB workgroups run
-// two per CU, so one covers the other's.  Measured on 32 experts, 16384
-// rows, K 2048, N 7168: 596 -> 550 us.  The FP8 modes ran 7-14% slower
-// with it (their operand bytes per flop double), and so do not use it.
+// Exact-mode products with short K (at most 16 chunks), dense and grouped:
+// with one workgroup per CU each tile's pipeline fill and C stores stand
+// alone, and the large tiles end on a partly filled round.  These 67 KB
+// workgroups run two per CU, so one covers the other's.  Measured (us):
+// grouped, 32 experts, 16384 rows, K 2048, N 7168: 596 -> 550; dense
+// 8192 x 7168 x 2048: 228 -> 218, 4096 x 7168 x 2048: 136 -> 112,
+// 8192 x 4096 x 1024: 77 -> 70, 16384 x 7168 x 2048: 441 -> 432.  The FP8
+// modes ran 7-14% slower with it (their operand bytes per flop double),
+// and so do not use it.
 using ShortKExactCfg = TileCfg<128, 128, 2, 2>;
+constexpr int64_t kShortK = 2048;
 using SplitCfg = TileCfg<64, 128, 1, 4, 3>;  // split-K, memory-bound small M: 3 stages, 2 per CU
 // Grouped GEMM with few rows per expert (decode batches): the expert weights
 // dominate the traffic.  64 x 128 tiles with full-height waves: a slot runs
@@ -1040,7 +1044,8 @@ size_t gemm_workspace_required(int64_t M, int64_t N, int64_t K) {
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   size_t b = gemm_workspace_required(M, N, K);
-  const size_t t0 = tail_bytes<BigExactCfg>(tail_plan<BigExactCfg>(M, N, K));
+  // exact products with short K take ShortKExactCfg, which is not split
+  const size_t t0 = K > kShortK ? tail_bytes<BigExactCfg>(tail_plan<BigExactCfg>(M, N, K)) : 0;
   const size_t t1 = tail_bytes<BigCfg>(tail_plan<BigCfg>(M, N, K));
   if (t0 > b) b = t0;
   if (t1 > b) b = t1;
@@ -1111,6 +1116,9 @@ static hipError_t gemm_dispatch(const uint8_t* qa, int64_t lda, const ScaleOf<MO
   const bool big = M > 128 && N % 256 == 0;
   if (p.S > 1) {
     launch_splitk<MODE>(p, qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, part, st);
+  } else if (MODE == 0 && K <= kShortK && M > 128) {
+    if constexpr (MODE == 0)
+      launch_dense<ShortKExactCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, st);
   } else if (big) {
     using C = DenseBigOf<MODE>;
     const TailPlan tp = tail_plan<C>(M, N, K);
@@ -1311,7 +1319,7 @@ static hipError_t grouped_dispatch(const uint8_t* qa, int64_t lda, const ScaleOf
   // from the sizes alone; offsets stay on the device)
   const bool decode = total_rows <= 128 * E && N % MoeDecodeCfg::BN == 0;
   if constexpr (MODE == 0) {
-    if (!decode && K <= 2048 && total_rows > 128) {
+    if (!decode && K <= kShortK && total_rows > 128) {
       launch_grouped<ShortKExactCfg, 0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, w_es, sw, sw_snb, sw_skb, sw_es,
                                         offsets, E, total_rows, c, ldc, N, K, st);
       return hipGetLastError();

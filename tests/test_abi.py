@@ -135,6 +135,10 @@ def test_gemm_validation(lib):
     assert lib.fgq_gemm_workspace_bytes(8192, 18432, 7168) == 24 * 10 * 192 * 256 * 4
     # a last round more than half full is not split
     assert lib.fgq_gemm_workspace_bytes(8064, 18432, 7168) == 0
+    # 2112 rows are 264 exact-mode tiles (one round and 8, split 5 ways at K 2560) and
+    # 216 FP8 tiles; with K at most 2048 the exact mode takes 128x128 tiles, unsplit
+    assert lib.fgq_gemm_workspace_bytes(2112, 6144, 2560) == 8 * 5 * 192 * 256 * 4
+    assert lib.fgq_gemm_workspace_bytes(2112, 6144, 2048) == 0
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL     # no workspace
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P + 16, ws_bytes=need) == ALIGN

@@ -368,12 +368,13 @@ def test_gemm_and_grouped_deterministic(fgq_gpu, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("M,N,K", [(2112, 6144, 1024), (2816, 6144, 2048)])
+@pytest.mark.parametrize("M,N,K", [(2112, 6144, 2560), (2816, 6144, 2560)])
 def test_gemm_last_round_split(fgq_gpu, M, N, K, mode):
     """Large products whose last round of tiles is split along K into
     partial sums in the workspace (2112 rows: the exact mode's 264 tiles are
-    one round and 8; 2816 rows: both modes, up to 4 parts): the tolerance
-    gate with the workspace, and without one (the plain launch)."""
+    one round and 8; 2816 rows: both modes, up to 5 parts): the tolerance
+    gate with the workspace, and without one (the plain launch).  K is above
+    2048, where the exact mode takes its large tiles."""
     import torch
     a = normal_bf16((M, K), 1.0, rng_for(41, M))
     w = normal_bf16((N, K), 0.02, rng_for(41, N))
