@@ -139,6 +139,14 @@ def test_gemm_validation(lib):
     # 216 FP8 tiles; with K at most 2048 the exact mode takes 128x128 tiles, unsplit
     assert lib.fgq_gemm_workspace_bytes(2112, 6144, 2560) == 8 * 5 * 192 * 256 * 4
     assert lib.fgq_gemm_workspace_bytes(2112, 6144, 2048) == 0
+    # the larger of the two modes' splits: 2816 rows are 360 exact-mode tiles (104 in
+    # the last round, 2 parts) and 264 FP8 tiles (8 in the last round, 5 parts at K 2560)
+    assert lib.fgq_gemm_workspace_bytes(2816, 6144, 2560) == 104 * 2 * 192 * 256 * 4
+    # parts are capped at 16 (and at a quarter of the K chunks)
+    assert lib.fgq_gemm_workspace_bytes(2112, 6144, 8192) == 8 * 16 * 192 * 256 * 4
+    assert lib.fgq_gemm_workspace_bytes(2112, 6144, 3072) == 8 * 6 * 192 * 256 * 4
+    # fewer tiles than compute units: one round, nothing to split
+    assert lib.fgq_gemm_workspace_bytes(1024, 6144, 7168) == 0
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL     # no workspace
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P + 16, ws_bytes=need) == ALIGN
