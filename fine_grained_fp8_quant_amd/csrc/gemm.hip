@@ -182,7 +182,7 @@ __device__ __forceinline__ int lds_col(int c, int r) { return c ^ (((r >> 3) & 1
 // scales applied by the unit (MODE 2 promote, MODE 3 in-core).  Lane
 // (l16, lgrp) feeds row l16 of a sub-tile with code bytes 32 lgrp ...
 // 32 lgrp + 31 of the chunk.
-template <class C, int MODE>
+template <class C, int MODE, bool LATE = true>
 struct Engine16 {
   v4f acc[C::TM][C::TN];
   int wm, wn, l16, lgrp;
@@ -359,6 +359,18 @@ struct Engine16 {
     for (int ni = 0; ni < C::TN; ++ni) fma4(arow[ni], t[ni], sc);
   }
 
+  // one sub-tile row's chunk sums, exact products, without the promotion
+  __device__ __forceinline__ void exact_mma(v4f (&t)[C::TN], const uint4& lo, const uint4& hi) {
+    const uint32_t aw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v8h a = e4m3x8_to_f16(aw[2 * ks], aw[2 * ks + 1]);
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni)
+        t[ni] = mfma_16x16x32_f16(a, bhm[ni][ks], ks == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : t[ni]);
+    }
+  }
+
   // binary32 scales: the chunk's FP32 sum, then promotion by the vector ALU
   template <int TMA>
   __device__ __forceinline__ void chunk_f32(const uint8_t* base) {
@@ -424,7 +436,15 @@ struct Engine16 {
       uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
       uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
       v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
-      exact_row(acc[TMA - 1], pa_lo, pa_hi, psc);  // the previous chunk's last row
+      // the previous chunk's last row.  With LATE, its promotion (and each
+      // row's below) is issued after the next row's matrix operations,
+      // behind a scheduling barrier, so no multiply-add waits on the
+      // operation that produces its input.
+      v4f tp[C::TN];
+      v4f sp = psc;
+      int rp = TMA - 1;  // the row whose promotion is pending
+      if constexpr (LATE) exact_mma(tp, pa_lo, pa_hi);
+      else exact_row(acc[TMA - 1], pa_lo, pa_hi, psc);
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) {
         uint4 lo, hi;
@@ -445,10 +465,32 @@ struct Engine16 {
         const uint4 nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
         const uint4 nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
         const v4f nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
-        exact_row(acc[mi], alo, ahi, (v4f){sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv});
+        const v4f sc = {sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv};
+        if constexpr (LATE) {
+          v4f tc[C::TN];
+          exact_mma(tc, alo, ahi);
+          __builtin_amdgcn_sched_barrier(0);
+          if (rp == TMA - 1) {
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], tp[ni], sp);
+          } else {
+#pragma unroll
+            for (int ni = 0; ni < C::TN; ++ni) fma4(acc[rp][ni], tp[ni], sp);
+          }
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) tp[ni] = tc[ni];
+          sp = sc;
+          rp = mi;
+        } else {
+          exact_row(acc[mi], alo, ahi, sc);
+        }
         alo = nlo;
         ahi = nhi;
         sa4 = nsa;
+      }
+      if constexpr (LATE) {
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) fma4(acc[rp][ni], tp[ni], sp);
       }
       pa_lo = alo;
       pa_hi = ahi;
@@ -787,7 +829,8 @@ __device__ __forceinline__ void gemm_tile_fused(const uint16_t* __restrict__ a, 
     }
   };
 
-  Engine16<C, MODE> eng(wave, lane);
+  // the exact engine's late promotion would spill here, beside the A ring
+  Engine16<C, MODE, false> eng(wave, lane);
   // A tiles travel two chunks ahead in a two-slot register ring: chunk k
   // lives in ring[(k - kb_begin) & 1].  Within an iteration the weight
   // request goes out before the A loads, and the prologue keeps that order,
