@@ -35,10 +35,11 @@ definition evaluated in float64.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, exhaustive enumeration or library
-routines, except the bit-level summation order of the fused RMSNorm (see
-``oracle.quant.rmsnorm_r64``), which is a reading the pages do not fix:
-its value is pinned to the float64 norm within the forward-error bound of
-that order, and the order itself is "parity unpinned" beyond that.
+routines.  The summation order of the fused RMSNorm
+(``oracle.quant.sum_squares_r64``) is a reading the pages do not fix; it is
+pinned by crafted rows whose hand-derived binary32 sums differ from those of
+a sequential sum, contiguous per-partial vectors, a reversed butterfly and a
+fused multiply-add accumulation.
 """
 from .e4m3 import (  # noqa: F401
     E4M3_MAX,
@@ -53,6 +54,7 @@ from .quant import (  # noqa: F401
     quant_act_1x128,
     quant_w_128x128,
     rmsnorm_r64,
+    sum_squares_r64,
 )
 from .gemm import (  # noqa: F401
     bf16_round_f64,

@@ -81,30 +81,24 @@ def quant_w_128x128(w_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return (q, s) if batched else (q[0], s[0])
 
 
-def rmsnorm_r64(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float) -> np.ndarray:
-    """RMSNorm ``y = x * rsqrt(mean(x**2) + eps) * gamma`` in binary32, in one
-    fixed evaluation order; returns float32 ``[M, K]`` (not rounded to BF16).
+def sum_squares_r64(x_bits: np.ndarray) -> np.ndarray:
+    """Sum of squares of each row of BF16 ``x [M, K]`` in the fixed order
+    "R64"; returns float32 ``[M]``.
 
     Reading: the pages say only that the normalisation stays in higher
-    precision and may be fused with the cast; the workload names RMSNorm
-    with ``eps = 1e-6`` and BF16 gamma.  A bit-exact answer needs one
-    summation order, fixed here ("R64"): the row is cut into vectors of 8
-    consecutive values; 64 partial sums each take every 64th vector in
-    turn (partial ``l`` takes vectors ``l, l+64, ...``) and add the squares
-    of its 8 values one by one, ``acc = fl32(acc + fl32(x*x))`` (no fused
-    multiply-add); the 64 partials are then combined by a butterfly, each
-    partial ``l`` adding partial ``l xor d`` for ``d = 32, 16, 8, 4, 2, 1``.
-    Then ``mean = fl32(ss / K)``, ``v = fl32(mean + fl32(eps))``,
-    ``rstd = fl32(1 / fl32(sqrt(v)))``, ``y = fl32(fl32(x * rstd) * gamma)``.
-    The order is "parity unpinned" beyond the agreement with the float64
-    norm, within the binary32 forward-error bound of this order, that the
-    tests check.
+    precision and may be fused with the cast; a bit-exact answer needs one
+    summation order, and this one is fixed here.  The row is cut into
+    vectors of 8 consecutive values.  64 partial sums each take every 64th
+    vector in turn (partial ``l`` takes vectors ``l, l+64, ...``) and add the
+    squares of its 8 values one by one, ``acc = fl32(acc + fl32(x*x))`` (a
+    multiply, then an add: no fused multiply-add).  The 64 partials are then
+    combined by a butterfly: for ``d = 32, 16, 8, 4, 2, 1`` every partial
+    ``l`` becomes ``fl32(acc_l + acc_(l xor d))``; the result is partial 0.
     """
     M, K = x_bits.shape
     if K % 8:
         raise ValueError("K must be a multiple of 8")
     x = f32_from_bf16(x_bits)
-    g = f32_from_bf16(gamma_bits)
     V = K // 8
     acc = np.zeros((M, 64), dtype=np.float32)
     xv = x.reshape(M, V, 8)
@@ -117,7 +111,24 @@ def rmsnorm_r64(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float) -> np.nd
     for d in (32, 16, 8, 4, 2, 1):
         partner = np.arange(64) ^ d
         acc = (acc + acc[:, partner]).astype(np.float32)
-    ss = acc[:, 0]
+    return acc[:, 0].copy()
+
+
+def rmsnorm_r64(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm ``y = x * rsqrt(mean(x**2) + eps) * gamma`` in binary32;
+    returns float32 ``[M, K]`` (not rounded to BF16).
+
+    The workload names RMSNorm with ``eps = 1e-6`` and BF16 gamma.  The sum
+    of squares is ``sum_squares_r64`` (one fixed order); then ``mean =
+    fl32(ss / K)``, ``v = fl32(mean + fl32(eps))``, ``rstd = fl32(1 /
+    fl32(sqrt(v)))``, ``y = fl32(fl32(x * rstd) * gamma)``.
+    """
+    M, K = x_bits.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    x = f32_from_bf16(x_bits)
+    g = f32_from_bf16(gamma_bits)
+    ss = sum_squares_r64(x_bits)
     mean = (ss / np.float32(K)).astype(np.float32)
     v = (mean + np.float32(eps)).astype(np.float32)
     rstd = (np.float32(1.0) / np.sqrt(v).astype(np.float32)).astype(np.float32)

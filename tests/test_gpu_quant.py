@@ -265,3 +265,22 @@ def test_fused_shapes(fgq_gpu, K):
     qo, so = oracle.fused_rmsnorm_quant(xb, gb, 1e-6)
     q, s = _fused(fgq_gpu, xb, gb, 1e-6, ldq=K + 16, scale_t=(K == 640))
     _assert_same(q, s, qo, so, f"fused K={K}")
+
+
+@pytest.mark.parametrize("K", [1024, 7168])
+def test_fused_r64_crafted_rows(fgq_gpu, K):
+    # the crafted rows that pin the oracle's summation order (their first 1024
+    # values; zeros after): where the order changes rstd, it changes the codes
+    # and scales, which must still match the oracle bit for bit
+    from tests.test_oracle_quant import _R64_CASES
+    rows = []
+    for make, _, _ in _R64_CASES:
+        x = np.zeros(K, np.float32)
+        x[:1024] = make()
+        rows.append(x)
+    x = np.stack(rows)
+    xb = bf16_bits_from_f32(x)
+    gb = bf16_bits_from_f32(np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32))
+    qo, so = oracle.fused_rmsnorm_quant(xb, gb, 1e-6)
+    q, s = _fused(fgq_gpu, xb, gb, 1e-6)
+    _assert_same(q, s, qo, so, f"fused crafted rows K={K}")

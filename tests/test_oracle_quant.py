@@ -9,7 +9,11 @@ Independent of the oracle's own arithmetic:
   * the E4M3 error bound on random data with outliers;
   * planted per-block maxima pin the 128x128 block indexing;
   * the fused RMSNorm: closed form on constant rows, and agreement with a
-    float64 RMSNorm within its binary32 forward-error bound on random rows (including a ragged lane tail).
+    float64 RMSNorm within its binary32 forward-error bound on random rows (including a ragged lane tail);
+  * its summation order: crafted rows whose hand-derived binary32 sums of
+    squares differ from a sequential sum, contiguous per-partial vectors, a
+    reversed butterfly, a fused multiply-add accumulation and a reversed
+    vector order within a partial.
 """
 import math
 from fractions import Fraction
@@ -18,7 +22,7 @@ import numpy as np
 import pytest
 
 from oracle import (e4m3_decode, fused_rmsnorm_quant, f32_from_bf16, quant_act_1x128,
-                    quant_w_128x128, rmsnorm_r64)
+                    quant_w_128x128, rmsnorm_r64, sum_squares_r64)
 from synth import bf16_bits_from_f32, normal_bf16, rng_for
 
 
@@ -283,3 +287,185 @@ def test_fused_equals_quant_of_rmsnorm_output_invariants():
     # y is not rounded to BF16 before the cast: differs from quantising bf16(y)
     qb, sb2 = quant_act_1x128(_bf16(y.astype(np.float32)))
     assert not (np.array_equal(q, qb) and np.array_equal(s, sb2))
+
+
+# ------------------------------------------- the R64 summation order, pinned
+#
+# Crafted rows (K = 1024, so 128 vectors of 8 values; in the R64 order partial
+# l takes vectors l and l + 64) whose binary32 sum of squares is derived by
+# hand below.  Each row is built so that one or more plausible alternative
+# orders round differently; the alternatives are evaluated by the small loops
+# in this test, written independently of the oracle.
+
+def _rne_f32(fr: Fraction) -> Fraction:
+    """Nearest binary32 value (subnormals included), ties to even, as a Fraction."""
+    if fr == 0:
+        return Fraction(0)
+    mag = abs(fr)
+    e = mag.numerator.bit_length() - mag.denominator.bit_length()
+    if Fraction(2) ** e > mag:
+        e -= 1
+    q = Fraction(2) ** (max(e, -126) - 23)      # spacing of the binade (subnormal: 2**-149)
+    n, r = divmod(mag, q)
+    n = int(n)
+    if r > q / 2 or (r == q / 2 and n % 2 == 1):
+        n += 1
+    return (n * q) if fr > 0 else -(n * q)
+
+
+def _f32(v) -> np.float32:
+    return np.float32(v)
+
+
+def _ss_loop(x, assign, ds, fused=False):
+    """Sum of squares of one float32 row: 64 partials, partial l adding the
+    squares of the vectors assign(l) one value at a time, then a butterfly over
+    the distances ds.  fused: each step rounds acc + x*x once (a fused
+    multiply-add) instead of rounding the square first."""
+    acc = [_f32(0.0)] * 64
+    for lane in range(64):
+        a = _f32(0.0)
+        for v in assign(lane):
+            for j in range(8):
+                xv = x[8 * v + j]
+                if fused:
+                    a = _f32(float(_rne_f32(Fraction(float(a)) + Fraction(float(xv)) ** 2)))
+                else:
+                    a = _f32(a + _f32(xv * xv))
+        acc[lane] = a
+    for d in ds:
+        acc = [_f32(acc[lane] + acc[lane ^ d]) for lane in range(64)]
+    return acc[0]
+
+
+def _ss_sequential(x):
+    a = _f32(0.0)
+    for xv in x:
+        a = _f32(a + _f32(xv * xv))
+    return a
+
+
+_V = 128  # vectors in a K = 1024 row
+_ALT = {
+    "sequential": _ss_sequential,
+    "contiguous partials": lambda x: _ss_loop(x, lambda l: range(2 * l, 2 * l + 2), (32, 16, 8, 4, 2, 1)),
+    "reversed butterfly": lambda x: _ss_loop(x, lambda l: (l, l + 64), (1, 2, 4, 8, 16, 32)),
+    "fused multiply-add": lambda x: _ss_loop(x, lambda l: (l, l + 64), (32, 16, 8, 4, 2, 1), fused=True),
+    "later vector first": lambda x: _ss_loop(x, lambda l: (l + 64, l), (32, 16, 8, 4, 2, 1)),
+}
+
+
+def _row_big_then_lane_eights():
+    # x_0 = 2**12 (square 2**24); in vectors 1..63 (first vectors of partials
+    # 1..63) every value is 1.
+    x = np.zeros(1024, np.float32)
+    x[0] = 4096.0
+    x[8:512] = 1.0
+    return x
+
+
+def _row_big_and_upper_half_ones():
+    # x_0 = 2**12; the first value of vectors 32..63 is 1 (partials 32..63
+    # hold 1 each).
+    x = np.zeros(1024, np.float32)
+    x[0] = 4096.0
+    x[8 * np.arange(32, 64)] = 1.0
+    return x
+
+
+def _row_ones_then_big():
+    # vector 0 all ones, then x_512 = 2**12 (first value of vector 64, the
+    # second vector of partial 0).
+    x = np.zeros(1024, np.float32)
+    x[0:8] = 1.0
+    x[512] = 4096.0
+    return x
+
+
+def _row_subnormal_tie():
+    # x_0 = 3 * 2**-76 (square 9 * 2**-152 = 1.125 * 2**-149), x_1 = 2**-75
+    # (square exactly 2**-150, half the smallest subnormal).
+    x = np.zeros(1024, np.float32)
+    x[0] = 3.0 * 2.0 ** -76
+    x[1] = 2.0 ** -75
+    return x
+
+
+# (row, hand-derived R64 sum, {alternative: its hand-derived sum}).  Every
+# listed alternative differs from the R64 sum.
+#
+# Row 1.  R64: partial 0 holds 2**24; partials 1..63 hold 8 (eight squares of
+# 1, exact).  Every butterfly sum is an even integer below 2**25, so exact:
+# 2**24 + 63 * 8 = 16777720.  Sequential: each later +1 meets 2**24, a tie
+# between 2**24 and 2**24 + 2, which rounds to even (2**24): 16777216.
+# Contiguous partials: partial 0 takes vectors 0 and 1, so the eight ones of
+# vector 1 are dropped one by one against 2**24; the other 62 vectors of ones
+# (31 partials of 16) arrive exactly: 2**24 + 496 = 16777712.
+#
+# Row 2.  R64: after d = 32, partial 0 is 2**24 + 1 -> 2**24 (tie, even),
+# partials 1..31 hold 1.  d = 16: 2**24 + 1 -> 2**24 again; partials 1..15
+# hold 2.  d = 8: 2**24 + 2 (exact); partials 1..7 hold 4.  d = 4: + 4 ->
+# 2**24 + 6; d = 2: + 8 -> 2**24 + 14; d = 1: + 16 -> 2**24 + 30 = 16777246.
+# Reversed butterfly: the 32 ones meet each other first (partials 32..63 reach
+# 32 by d = 16), partial 0 stays 2**24 until d = 32 adds 32: 16777248.
+# Sequential: every one is dropped: 16777216.  Contiguous partials: vectors
+# 32..63 land in partials 16..31 (2 each); d = 32 adds zeros, then d = 16
+# adds 2, d = 8 adds 2, d = 4 adds 4, d = 2 adds 8, d = 1 adds 16: 16777248.
+#
+# Row 3.  R64: partial 0 adds the eight ones (8), then 2**24: 2**24 + 8 =
+# 16777224 (exact).  Taking the later vector first gives 2**24, then eight
+# dropped ones: 16777216.
+#
+# Row 4.  R64: fl32(x_0**2) = 2**-149 (1.125 units of 2**-149 round to 1);
+# fl32(x_1**2) = 0 (half a unit, a tie, rounds to even 0); the sum is 2**-149.
+# Fused multiply-add: the first step gives 2**-149, the second rounds
+# 2**-149 + 2**-150 = 1.5 units, a tie, to even: 2 units = 2**-148.
+_R64_CASES = [
+    (_row_big_then_lane_eights, 16777720.0,
+     {"sequential": 16777216.0, "contiguous partials": 16777712.0}),
+    (_row_big_and_upper_half_ones, 16777246.0,
+     {"reversed butterfly": 16777248.0, "sequential": 16777216.0, "contiguous partials": 16777248.0}),
+    (_row_ones_then_big, 16777224.0, {"later vector first": 16777216.0}),
+    (_row_subnormal_tie, 2.0 ** -149, {"fused multiply-add": 2.0 ** -148}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(_R64_CASES)))
+def test_r64_order_pinned_by_crafted_rows(case):
+    make, want, alternatives = _R64_CASES[case]
+    x = make()
+    xb = _bf16(x)
+    assert np.array_equal(f32_from_bf16(xb), x), "crafted values must be exact in BF16"
+    ss = sum_squares_r64(xb[None, :])[0]
+    assert ss.dtype == np.float32
+    assert float(ss) == want, (float(ss), want)
+    for name, alt_want in alternatives.items():
+        got = float(_ALT[name](x))
+        assert got == alt_want, (name, got, alt_want)   # the alternative loop agrees with its derivation
+        assert got != want, name                       # ... and R64 tells it apart
+
+
+def test_r64_alternatives_all_rejected():
+    # every alternative order is told apart from R64 by at least one crafted row
+    rejected = set()
+    for _, _, alternatives in _R64_CASES:
+        rejected |= set(alternatives)
+    assert rejected == set(_ALT)
+
+
+def test_rmsnorm_uses_the_r64_sum():
+    # row 1 through the whole norm: with gamma = 1 the output at a value of 1
+    # is rstd itself, which the R64 sum (not the sequential one) determines
+    x = _row_big_then_lane_eights()
+    xb = _bf16(x)[None, :]
+    gb = _bf16(np.ones(1024, np.float32))
+    y = rmsnorm_r64(xb, gb, 1e-6)
+
+    def rstd_of(ss):
+        mean = round_f32(Fraction(ss) / 1024)
+        v = round_f32(Fraction(float(mean)) + Fraction(float(np.float32(1e-6))))
+        return round_f32(1 / Fraction(float(sqrt_f32(v))))
+
+    assert y[0, 8] == rstd_of(16777720.0)
+    assert rstd_of(16777720.0) != rstd_of(16777216.0)
+    assert np.array_equal(y[0], (x * y[0, 8]).astype(np.float32))
