@@ -282,7 +282,48 @@ def make_step(args, fgq, d, n_sets, mode):
         else:
             t.run(nm["grouped"], lambda: api.grouped(o["qa"], o["sa"], o["qw"], o["sw"], s["off"], out=o["c"],
                                                      mode=mode))
+    step.outputs = outs
     return step
+
+
+def measured_ceilings(fgq):
+    """The matrix cores' sustained rate on register-only loops over every
+    SIMD (two waves each), and the shader clock the waves measured meanwhile:
+    the ceiling this box reaches, beside the nominal peaks."""
+    import torch
+    out = {}
+    fgq.debug_mfma_loop(0, 200)                    # wake the clocks
+    for kind, key in ((0, "mfma_fp8_tflops"), (1, "mfma_fp16_tflops"), (2, "mfma_fp16_32x32_tflops")):
+        r = fgq.debug_mfma_loop(kind, 4000 if kind == 0 else 8000, waves=2048)
+        out[key] = r["tflops"]
+        out[key.replace("tflops", "sclk_ghz")] = r["sclk_ghz"]
+    torch.cuda.synchronize()
+    out["note"] = ("register-only MFMA loops, 2048 waves (two per SIMD), 8 independent operations per round; "
+                   "clock = s_memtime / s_memrealtime (100 MHz) over the loop")
+    return out
+
+
+def bf16_product_error(args, d, s0, c):
+    """Normwise error of the step's BF16 output against the float64 product of
+    the unquantised BF16 operands, on sampled rows (reported, not gated)."""
+    import torch
+    rng = np.random.default_rng(1)
+    if args.workload in ("prefill", "decode"):
+        A, W = s0["A"], s0["W"]
+        rows = np.sort(rng.choice(A.shape[0], min(64, A.shape[0]), replace=False))
+        ref = A[rows].double() @ W.double().t()
+        got = c[rows].double()
+    elif args.workload in ("grouped_up", "fused_down"):
+        A, W, off = s0["A"], s0["W"], d["offsets"]
+        rows = np.sort(rng.choice(A.shape[0], 64, replace=False))
+        expert = np.searchsorted(off, rows, side="right") - 1
+        ref = torch.stack([A[int(r)].double() @ W[int(e)].double().t() for r, e in zip(rows, expert)])
+        got = c[rows].double()
+    else:
+        return None   # dispatch workloads: rows are expert-ordered copies of token rows
+    err = float(torch.linalg.norm(got - ref) / torch.linalg.norm(ref))
+    return {"normwise_vs_unquantised_bf16_product": err, "rows_sampled": len(rows),
+            "note": "float64 product of the BF16 operands; reported, not gated"}
 
 
 CPU_TARGET_S = 10.0   # the oracle's sample grows in whole units until it has run this long
@@ -299,11 +340,23 @@ def cpu_baseline(args, d):
     gemm_ref = oracle.gemm_e8m0_ref if e8 else oracle.gemm_ref
     q_disp = oracle.quant_dispatch_e8m0_ref if e8 else oracle.quant_dispatch_ref
     fused = oracle.fused_rmsnorm_quant_e8m0 if e8 else oracle.fused_rmsnorm_quant
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas_threads = max([p.get("num_threads", 1) for p in blas] or [1])
+        blas_name = ",".join(sorted({p.get("internal_api", "?") for p in blas})) or "?"
     except Exception:
-        blas_threads = 1
+        blas_threads, blas_name = 1, "?"
+    cpu_model = "?"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     t0 = time.perf_counter()
     flops = 0.0
     if args.workload in ("prefill", "decode"):
@@ -349,10 +402,11 @@ def cpu_baseline(args, d):
                   + ("dispatch quant" if args.workload in ("dispatch", "moe_decode") else "quant A")
                   + ", quant W_e, float64 GEMM")
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS"
-                      + ("; E8M0 scales" if e8 else ""),
-            "seconds": dt}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(blas_threads, 1)), "kind": "oracle",
+            "sample": sample + f"; {dt:.1f} s; quantisation single-threaded NumPy, GEMM float64 BLAS ({blas_name}, "
+                      f"{blas_threads} threads)" + ("; E8M0 scales" if e8 else ""),
+            "seconds": dt, "host_cores_available": cores, "cpu_model": cpu_model, "blas": blas_name,
+            "blas_threads": int(blas_threads), "quant_threads": 1}
 
 
 def traffic_for(kernel):
@@ -403,10 +457,14 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
     kern = timer.avg_ms()
+    last_c = step.outputs[0]["c"]
+    ceilings = measured_ceilings(fgq)
     gemm_name = [k for k in kern if "gemm" in k][0]
     gemm_ms = kern[gemm_name]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
-    peak = PEAK_FP16_TFLOPS if args.mode == "exact" else PEAK_FP8_TFLOPS   # e8m0 modes run on the FP8 cores
+    # the contraction's own matrix-core dtype: exact products run on the FP16
+    # cores, the other modes on the FP8 cores
+    dtype_peak = PEAK_FP16_TFLOPS if args.mode == "exact" else PEAK_FP8_TFLOPS
     kernels = {}
     for k, ms in kern.items():
         if "gemm" in k:
@@ -429,12 +487,17 @@ def main():
         roofline = {"bound": "hbm", "kernel": gemm_name, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": gbytes, "traffic": traffic}
     else:
-        roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                    "frac": achieved / peak,
-                    "peak_note": "dense MFMA peak of the contraction's own dtype ("
-                                 + ("fp16" if args.mode == "exact" else "fp8") + ")",
+        ceiling = ceilings.get("mfma_fp16_tflops" if args.mode == "exact" else "mfma_fp8_tflops")
+        roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
+                    "peak_note": "dense FP8 MFMA peak (the metric's); the exact mode's products run on the "
+                                 "FP16 matrix cores" if args.mode == "exact" else "dense FP8 MFMA peak",
+                    "frac_contraction_dtype_peak": achieved / dtype_peak,
+                    "contraction_dtype": "fp16" if args.mode == "exact" else "fp8",
+                    "frac_measured_ceiling": achieved / ceiling if ceiling else None,
                     "traffic": traffic}
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    accuracy = bf16_product_error(args, d, sets[0], last_c)
     # the other GEMM accumulation mode, timed alone (not part of the step)
     other = {"exact": "fp8core", "fp8core": "exact", "promote": "incore", "incore": "promote"}[args.mode]
     alt_step = make_step(args, fgq, d, len(sets), gemm_mode(fgq, other))
@@ -473,6 +536,8 @@ def main():
         "gemm_mode": args.mode,
         "gemm_other_mode": alt,
         "cpu_baseline": cpu,
+        "accuracy": accuracy,
+        "ceilings": ceilings,
         "wall_s_timed": wall,
     }
     print(json.dumps(line), flush=True)

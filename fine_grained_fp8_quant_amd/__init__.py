@@ -43,7 +43,7 @@ __all__ = [
     "debug_encode_e4m3", "debug_copy", "debug_mfma_16x16x128", "STATUS", "GEMM_EXACT", "GEMM_FP8_CORE",
     "quant_act_1x128_e8m0", "quant_w_128x128_e8m0", "fused_rmsnorm_quant_e8m0", "act_scales_e8m0",
     "gemm_fp8_e8m0", "grouped_gemm_fp8_e8m0", "debug_mfma_e8m0_16x16x128", "E8M0_PROMOTE", "E8M0_IN_CORE",
-    "quant_dispatch_1x128_e8m0", "gemm_bf16a_fp8_blockscaled",
+    "quant_dispatch_1x128_e8m0", "gemm_bf16a_fp8_blockscaled", "debug_mfma_loop", "MFMA_LOOP_FLOPS",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +103,7 @@ _SIGNATURES = {
     "fgq_grouped_gemm_fp8_e8m0": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                   _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _st, _vp],
     "fgq_debug_mfma_e8m0_16x16x128": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "fgq_debug_mfma_loop": [_st, _i64, _i64, _vp, _vp, _vp],
     "fgq_gemm_bf16a_fp8_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _st,
                                        _vp, _i64, _vp, _i64, _i64, _vp, ctypes.c_size_t, _vp],
     "fgq_quant_dispatch_1x128_e8m0": [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
@@ -154,6 +155,27 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _scoped(fn):
+    """Run a call helper (its last positional argument is the caller's stream,
+    or None) with that stream current, so the outputs and scratch buffers it
+    allocates come from that stream's pool and are not handed to another
+    stream while the call's kernels still use them."""
+    import functools
+
+    @functools.wraps(fn)
+    def run(*args):
+        stream = args[-1]
+        if stream is None:
+            return fn(*args)
+        with _torch().cuda.stream(stream):
+            return fn(*args)
+    return run
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
@@ -200,6 +222,7 @@ def act_scales_e8m0(M: int, K: int, device):
     return act_scales(M, K, device, _torch().uint8)
 
 
+@_scoped
 def _quant_act(fn, sdtype, x, q, s, stream):
     torch = _torch()
     load_library()
@@ -228,6 +251,7 @@ def quant_act_1x128_e8m0(x, q=None, s=None, stream=None):
     return _quant_act(lib.fgq_quant_act_1x128_e8m0, _torch().uint8, x, q, s, stream)
 
 
+@_scoped
 def _quant_w(fn, sdtype, w, q, s, stream):
     torch = _torch()
     load_library()
@@ -261,6 +285,7 @@ def quant_w_128x128_e8m0(w, q=None, s=None, stream=None):
     return _quant_w(lib.fgq_quant_w_128x128_e8m0, _torch().uint8, w, q, s, stream)
 
 
+@_scoped
 def _fused(fn, sdtype, x, gamma, eps, q, s, stream):
     torch = _torch()
     load_library()
@@ -317,6 +342,7 @@ def quant_dispatch_1x128_e8m0(x, ids, n_experts: int, q=None, s=None, offsets=No
                      dest, workspace, stream)
 
 
+@_scoped
 def _dispatch(fn, sdtype, x, ids, n_experts, q, s, offsets, row_src, dest, workspace, stream):
     torch = _torch()
     _need(x, torch.bfloat16, "x")
@@ -341,7 +367,7 @@ def _dispatch(fn, sdtype, x, ids, n_experts, q, s, offsets, row_src, dest, works
     need = quant_dispatch_workspace_bytes(T, topk, n_experts, K)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_bytes = _nbytes(workspace)
     _check(fn(_ptr(x), x.stride(0), T, K, _ptr(ids), topk, n_experts, _ptr(q), q.stride(0), _ptr(s), s.stride(0),
               s.stride(1), _ptr(offsets), _ptr(row_src), _ptr(dest), _ptr(workspace), ws_bytes, _stream(stream)))
     return q, s, offsets, row_src, dest
@@ -367,6 +393,7 @@ def gemm_fp8_e8m0(qa, sa, qw, sw, out=None, workspace=None, accumulate=E8M0_PROM
     return _gemm(lib.fgq_gemm_fp8_e8m0, _torch().uint8, qa, sa, qw, sw, out, workspace, accumulate, stream)
 
 
+@_scoped
 def _gemm(fn, sdtype, qa, sa, qw, sw, out, workspace, mode, stream):
     torch = _torch()
     qa, qw = _codes(qa), _codes(qw)
@@ -383,7 +410,7 @@ def _gemm(fn, sdtype, qa, sa, qw, sw, out, workspace, mode, stream):
     need = gemm_workspace_bytes(M, N, K)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qa.device)
-    ws_bytes = workspace.numel() if workspace is not None else 0
+    ws_bytes = _nbytes(workspace)
     _check(fn(_ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(0), _ptr(sw),
               sw.stride(0), sw.stride(1), _ptr(out), out.stride(0), M, N, K, int(mode), _ptr(workspace), ws_bytes,
               _stream(stream)))
@@ -395,6 +422,11 @@ def gemm_bf16a_fp8_blockscaled(a, qw, sw, out=None, workspace=None, mode=GEMM_EX
     """GEMM of BF16 ``a [M, K]`` with quantised weights, the 1x128 quantisation of
     ``a`` done inside the GEMM's A-load.  Optional ``qa_out`` (uint8 [M, K]) and
     ``sa_out`` (float32 [M, K/128] view) receive the codes and scales."""
+    return _gemm_bf16a(a, qw, sw, out, workspace, mode, qa_out, sa_out, stream)
+
+
+@_scoped
+def _gemm_bf16a(a, qw, sw, out, workspace, mode, qa_out, sa_out, stream):
     torch = _torch()
     load_library()
     qw = _codes(qw)
@@ -414,7 +446,7 @@ def gemm_bf16a_fp8_blockscaled(a, qw, sw, out=None, workspace=None, mode=GEMM_EX
     need = gemm_workspace_bytes(M, N, K)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
-    ws_bytes = workspace.numel() if workspace is not None else 0
+    ws_bytes = _nbytes(workspace)
     _check(lib.fgq_gemm_bf16a_fp8_blockscaled(
         _ptr(a), a.stride(0), _ptr(qw), qw.stride(0), _ptr(sw), sw.stride(0), sw.stride(1), _ptr(out), out.stride(0),
         M, N, K, int(mode), _ptr(qa_out), qa_out.stride(0) if qa_out is not None else 0, _ptr(sa_out),
@@ -439,6 +471,7 @@ def grouped_gemm_fp8_e8m0(qa, sa, qw, sw, offsets, out=None, accumulate=E8M0_PRO
                     stream)
 
 
+@_scoped
 def _grouped(fn, sdtype, qa, sa, qw, sw, offsets, out, mode, stream):
     torch = _torch()
     qa, qw = _codes(qa), _codes(qw)
@@ -494,6 +527,34 @@ def debug_mfma_e8m0_16x16x128(a, b, sa, sb, cin=None, stream=None):
     _check(lib.fgq_debug_mfma_e8m0_16x16x128(_ptr(a.contiguous()), _ptr(b.contiguous()), _ptr(sa.contiguous()),
                                              _ptr(sb.contiguous()), _ptr(cin.contiguous()), _ptr(d), _stream(stream)))
     return d
+
+
+MFMA_LOOP_FLOPS = {0: 65536, 1: 16384, 2: 32768}   # per operation of each fgq_debug_mfma_loop kind
+_MFMA_LOOP_OPS = {0: 8, 1: 8, 2: 8}                # operations per wave per round
+
+
+def debug_mfma_loop(kind: int, iters: int, waves: int = 2048, stream=None):
+    """Run fgq_debug_mfma_loop once; returns a dict with the elapsed time
+    (HIP events, ms), the matrix-core rate (TFLOP/s) over the whole launch,
+    and the shader clock (GHz) the waves measured while they ran."""
+    torch = _torch()
+    load_library()
+    with (torch.cuda.stream(stream) if stream is not None else __import__("contextlib").nullcontext()):
+        out = torch.zeros(4 * waves, dtype=torch.int64, device="cuda")
+        sink = torch.empty(64 * waves, dtype=torch.float32, device="cuda")
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        _check(lib.fgq_debug_mfma_loop(int(kind), int(iters), int(waves), _ptr(out), _ptr(sink), _stream(stream)))
+        e1.record(st)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    t = out.view(waves, 4).cpu().numpy().astype(float)
+    clk = (t[:, 1] - t[:, 0]).sum()
+    real = (t[:, 3] - t[:, 2]).sum()
+    flops = float(waves) * iters * _MFMA_LOOP_OPS[kind] * MFMA_LOOP_FLOPS[kind]
+    return {"kind": int(kind), "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "sclk_ghz": clk / real * 0.1 if real > 0 else float("nan"), "waves": int(waves), "iters": int(iters)}
 
 
 def debug_copy(src, dst, stream=None):

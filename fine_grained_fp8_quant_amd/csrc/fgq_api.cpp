@@ -13,6 +13,10 @@ namespace {
 thread_local int32_t g_last_hip_error = 0;
 
 constexpr int64_t kMaxTiles = (int64_t)1 << 31;  // 32-bit tile indices in the kernels
+// The GEMM kernels address a tile's operand rows by 32-bit byte offsets from
+// the tile's first row: row (at most 255) * ld + column (at most 112), which
+// stays below 2^32 for every ld <= 2^24 bytes.
+constexpr int64_t kMaxOperandLd = (int64_t)1 << 24;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -49,7 +53,7 @@ fgq_status_t check_gemm_common(const void* qa, int64_t lda, const void* sa, int6
   if (lda < K || lda % 16 != 0 || ldw < K || ldw % 16 != 0 || ldc < N || ldc % 8 != 0)
     return FGQ_ERR_STRIDE;
   if (sa_sm < 0 || sa_skb < 0 || sw_snb < 0 || sw_skb < 0) return FGQ_ERR_STRIDE;
-  if (N / 128 > 65535) return FGQ_ERR_UNSUPPORTED;
+  if (N / 128 > 65535 || lda > kMaxOperandLd || ldw > kMaxOperandLd) return FGQ_ERR_UNSUPPORTED;
   return FGQ_OK;
 }
 
@@ -204,7 +208,9 @@ fgq_status_t fgq_gemm_bf16a_fp8_blockscaled(const void* a, int64_t lda, const vo
   if (!aligned(a, 16) || !aligned(qw, 16) || !aligned(c, 16) || !aligned(sw, 4)) return FGQ_ERR_ALIGN;
   if (lda < K || lda % 8 != 0 || ldw < K || ldw % 16 != 0 || ldc < N || ldc % 8 != 0) return FGQ_ERR_STRIDE;
   if (sw_snb < 0 || sw_skb < 0) return FGQ_ERR_STRIDE;
-  if (lda > ((int64_t)1 << 23) || N / 128 > 65535 || M >= kMaxTiles) return FGQ_ERR_UNSUPPORTED;
+  // BF16 A: its rows are 2 * lda bytes apart
+  if (2 * lda > kMaxOperandLd || ldw > kMaxOperandLd || N / 128 > 65535 || M >= kMaxTiles)
+    return FGQ_ERR_UNSUPPORTED;
   if (qa_out) {
     if (!aligned(qa_out, 16) || !aligned(sa_out, 4)) return FGQ_ERR_ALIGN;
     if (ldq < K || ldq % 16 != 0 || sa_sm < 0 || sa_skb < 0) return FGQ_ERR_STRIDE;
@@ -388,6 +394,16 @@ fgq_status_t fgq_debug_mfma_e8m0_16x16x128(const void* a, const void* b, const u
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(cin, 4) || !aligned(d, 4)) return FGQ_ERR_ALIGN;
   return from_hip(fgq::launch_debug_mfma_e8m0(static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), sa, sb,
                                               cin, d, as_stream(stream)));
+}
+
+fgq_status_t fgq_debug_mfma_loop(int32_t kind, int64_t iters, int64_t waves, uint64_t* out, float* sink,
+                                 void* stream) {
+  if (kind < 0 || kind > 2) return FGQ_ERR_UNSUPPORTED;
+  if (iters < 0 || waves < 0 || waves % 4 != 0 || waves / 4 > 65535) return FGQ_ERR_SHAPE;
+  if (waves == 0) return FGQ_OK;
+  if (!out || !sink) return FGQ_ERR_NULL;
+  if (!aligned(out, 8) || !aligned(sink, 4)) return FGQ_ERR_ALIGN;
+  return from_hip(fgq::launch_debug_mfma_loop(kind, iters, waves, out, sink, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -84,6 +84,8 @@ hipError_t launch_gemm_bf16a_fp8_blockscaled(const uint16_t* a, int64_t lda, con
 hipError_t launch_debug_encode_e4m3(uint32_t start, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_debug_mfma(const uint8_t* a, const uint8_t* b, const float* cin, float* d, hipStream_t st);
+hipError_t launch_debug_mfma_loop(int kind, int64_t iters, int64_t waves, uint64_t* out, float* sink,
+                                  hipStream_t st);
 hipError_t launch_debug_mfma_e8m0(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
                                  const float* cin, float* d, hipStream_t st);
 

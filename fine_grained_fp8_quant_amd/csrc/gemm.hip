@@ -1455,4 +1455,82 @@ hipError_t launch_debug_mfma_e8m0(const uint8_t* a, const uint8_t* b, const uint
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Diagnostic: the matrix cores' sustained rate and the shader clock under
+// load.  Every wave runs `iters` rounds of 8 independent matrix operations on
+// register operands (no memory traffic in the loop) and records the shader
+// clock counter (s_memtime) and the constant 100 MHz counter (s_memrealtime)
+// before and after, so the host gets both the operation rate and the clock
+// the chip held while running it.  kind 0: v_mfma_f32_16x16x128_f8f6f4 (FP8,
+// 65536 flops); 1: v_mfma_f32_16x16x32_f16 (16384 flops); 2:
+// v_mfma_f32_32x32x16_f16 (32768 flops).  out[4 * wave + 0..3] = clock start,
+// clock end, real start, real end; sink receives a reduction of the results.
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_debug_mfma_loop(int64_t iters, uint64_t* __restrict__ out,
+                                                         float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  // operands from the lane id so the compiler cannot fold them
+  const int seed = lane * 0x01010101 + 0x3C3C3C3C;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  float red = 0.0f;
+  if constexpr (KIND == 0) {
+    const v8i a = (v8i){seed, seed ^ 1, seed ^ 2, seed ^ 3, seed ^ 4, seed ^ 5, seed ^ 6, seed ^ 7};
+    const v8i b = (v8i){seed ^ 8, seed ^ 9, seed ^ 10, seed ^ 11, seed ^ 12, seed ^ 13, seed ^ 14, seed ^ 15};
+    v4f acc[8];
+    for (int j = 0; j < 8; ++j) acc[j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j], 0, 0, 0, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) red += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  } else if constexpr (KIND == 1) {
+    const _Float16 h = (_Float16)(float)(lane & 7);
+    const v8h a = (v8h){h, h, h, h, h, h, h, h};
+    const v8h b = (v8h){h, (_Float16)1.0f, h, h, h, h, h, h};
+    v4f acc[8];
+    for (int j = 0; j < 8; ++j) acc[j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) red += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  } else {
+    const _Float16 h = (_Float16)(float)(lane & 7);
+    const v8h a = (v8h){h, h, h, h, h, h, h, h};
+    const v8h b = (v8h){h, (_Float16)1.0f, h, h, h, h, h, h};
+    v16f acc[4];
+    for (int j = 0; j < 4; ++j)
+      for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+    for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+      }
+    for (int j = 0; j < 4; ++j)
+      for (int e = 0; e < 16; ++e) red += acc[j][e];
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) {
+    out[4 * wave + 0] = c0;
+    out[4 * wave + 1] = c1;
+    out[4 * wave + 2] = r0;
+    out[4 * wave + 3] = r1;
+  }
+  sink[(int64_t)wave * 64 + lane] = red;
+}
+
+hipError_t launch_debug_mfma_loop(int kind, int64_t iters, int64_t waves, uint64_t* out, float* sink,
+                                  hipStream_t st) {
+  const dim3 grid((uint32_t)(waves / 4));
+  if (kind == 0) hipLaunchKernelGGL(k_debug_mfma_loop<0>, grid, dim3(256), 0, st, iters, out, sink);
+  else if (kind == 1) hipLaunchKernelGGL(k_debug_mfma_loop<1>, grid, dim3(256), 0, st, iters, out, sink);
+  else hipLaunchKernelGGL(k_debug_mfma_loop<2>, grid, dim3(256), 0, st, iters, out, sink);
+  return hipGetLastError();
+}
+
 }  // namespace fgq

@@ -152,10 +152,12 @@ enum { FGQ_GEMM_EXACT = 0, FGQ_GEMM_FP8_CORE = 1 };
  * P4 paragraph 4, P1 paragraph 4]; the result is rounded to BF16 (nearest even).
  *
  *   qa     E4M3 [M, K] (1x128-quantised activations), row stride lda (>= K,
- *          multiple of 16); 16-byte aligned.
+ *          multiple of 16, at most 2^24); 16-byte aligned.
  *   sa     float, sa[m * sa_sm + kb * sa_skb].
  *   qw     E4M3 [N, K] (128x128-quantised weights), row stride ldw (>= K,
- *          multiple of 16); 16-byte aligned.
+ *          multiple of 16, at most 2^24); 16-byte aligned.
+ *          (The kernels address operand rows by 32-bit offsets inside a
+ *          tile; a larger lda or ldw returns FGQ_ERR_UNSUPPORTED.)
  *   sw     float, sw[nb * sw_snb + kb * sw_skb].
  *   c      BF16 [M, N] output, row stride ldc (>= N, multiple of 8); 16-byte aligned.
  *   mode   FGQ_GEMM_EXACT or FGQ_GEMM_FP8_CORE (anything else: FGQ_ERR_UNSUPPORTED).
@@ -226,6 +228,7 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
  * fgq_gemm_fp8_blockscaled with the same mode.
  *
  *   a       BF16 [M, K], row stride lda (>= K, multiple of 8, at most 2^23); 16-byte aligned.
+ *           ldw at most 2^24, as in fgq_gemm_fp8_blockscaled.
  *   qw, sw, c, M, N, K, mode, workspace: as in fgq_gemm_fp8_blockscaled
  *           (the same fgq_gemm_workspace_bytes).
  *   qa_out, sa_out  optional (both NULL or both set): the codes and scales
@@ -417,6 +420,25 @@ fgq_status_t fgq_debug_copy(const void* src, void* dst, int64_t bytes, void* str
  * aligned), cin and d float [16][16] row-major.  Used to measure how the unit
  * accumulates a 128-wide chunk (the pages report ~14 retained bits on H800). */
 fgq_status_t fgq_debug_mfma_16x16x128(const void* a, const void* b, const float* cin, float* d, void* stream);
+
+/* fgq_debug_mfma_loop -- the matrix cores' sustained rate and the shader
+ * clock under that load, the measured ceiling beside the nominal peaks (the
+ * pages report no kernel-level throughput, so the chip's own limits are the
+ * reference for every roofline fraction).  `waves` waves (a multiple of 4,
+ * four per 256-thread workgroup) each run `iters` rounds of 8 independent
+ * register-only matrix operations of one kind:
+ *   kind 0  v_mfma_f32_16x16x128_f8f6f4  (FP8,  65536 flops each)
+ *   kind 1  v_mfma_f32_16x16x32_f16      (FP16, 16384 flops each)
+ *   kind 2  v_mfma_f32_32x32x16_f16      (FP16, 32768 flops each)
+ * out     DEVICE uint64 [4 * waves], 8-byte aligned: per wave the shader
+ *         clock counter (s_memtime) before and after the loop, then the
+ *         100 MHz real-time counter (s_memrealtime) before and after.
+ * sink    DEVICE float [64 * waves]: a reduction of the results (keeps the
+ *         work from being optimised away; its values mean nothing).
+ * Errors: kind outside 0..2 -> FGQ_ERR_UNSUPPORTED; iters < 0, waves < 0,
+ * waves not a multiple of 4 or above 4 * 65535 -> FGQ_ERR_SHAPE. */
+fgq_status_t fgq_debug_mfma_loop(int32_t kind, int64_t iters, int64_t waves, uint64_t* out, float* sink,
+                                 void* stream);
 
 /* fgq_debug_mfma_e8m0_16x16x128 -- one scaled FP8 matrix-core operation as
  * the E8M0 GEMMs issue it: d = diag(2^(sa - 127)) a b^T diag(2^(sb - 127)) + cin,

@@ -125,6 +125,13 @@ def test_gemm_validation(lib):
     assert gemm(lib, ldw=264) == STRIDE
     assert gemm(lib, ldc=128) == STRIDE
     assert gemm(lib, sa_skb=-1) == STRIDE
+    # operand rows are addressed by 32-bit offsets inside a tile: strides
+    # above 2^24 bytes would wrap them
+    assert gemm(lib, lda=(1 << 24) + 16) == UNSUP
+    assert gemm(lib, ldw=(1 << 24) + 16) == UNSUP
+    assert gemm(lib, lda=1 << 40) == UNSUP
+    assert lib.fgq_gemm_fp8_e8m0(P, 256, S, 2, 1, Q, (1 << 24) + 16, S, 2, 1, Q, 256, 4, 256, 256, 0, 0, 0,
+                                 None) == UNSUP
     assert lib.fgq_gemm_workspace_bytes(0, 256, 256) == 0
     # small M (memory-bound) shapes split K and need an FP32 workspace
     need = lib.fgq_gemm_workspace_bytes(64, 18432, 7168)
@@ -152,8 +159,8 @@ def test_gemm_validation(lib):
     assert gemm(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P + 16, ws_bytes=need) == ALIGN
 
 
-def grouped(lib, E=4, R=100, offsets=S, w_es=256 * 256, N=256, K=256, qa=P, ldc=256, mode=0):
-    return lib.fgq_grouped_gemm_fp8_blockscaled(qa, 256, S, 2, 1, Q, 256, w_es, S, 2, 1, 4, offsets, E, R,
+def grouped(lib, E=4, R=100, offsets=S, w_es=256 * 256, N=256, K=256, qa=P, ldc=256, mode=0, lda=256, ldw=256):
+    return lib.fgq_grouped_gemm_fp8_blockscaled(qa, lda, S, 2, 1, Q, ldw, w_es, S, 2, 1, 4, offsets, E, R,
                                                 Q, ldc, N, K, mode, None)
 
 
@@ -170,6 +177,8 @@ def test_grouped_validation(lib):
     assert grouped(lib, offsets=S + 2) == ALIGN
     assert grouped(lib, w_es=100 * 16) == STRIDE
     assert grouped(lib, ldc=128) == STRIDE
+    assert grouped(lib, lda=(1 << 24) + 16) == UNSUP
+    assert grouped(lib, ldw=(1 << 24) + 16, w_es=256 * ((1 << 24) + 16)) == UNSUP
 
 
 def test_debug_validation(lib):
@@ -313,6 +322,8 @@ def test_gemm_bf16a_validation(lib):
     assert gemm16(lib, a=P + 8) == ALIGN
     assert gemm16(lib, qa=Q + 8, sa=S) == ALIGN
     assert gemm16(lib, lda=128) == STRIDE
+    assert gemm16(lib, lda=(1 << 23) + 8) == UNSUP
+    assert gemm16(lib, ldw=(1 << 24) + 16) == UNSUP
     assert gemm16(lib, lda=260) == STRIDE
     assert gemm16(lib, qa=Q, sa=S, ldq=264) == STRIDE
     assert gemm16(lib, lda=(1 << 23) + 8, K=256) == UNSUP

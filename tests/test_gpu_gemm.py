@@ -389,3 +389,36 @@ def test_gemm_last_round_split(fgq_gpu, M, N, K, mode):
     torch.cuda.synchronize()
     _check(host_bf16_f64(c_split), ref, f"last-round split {M}x{N}x{K}", mode, qa, sa, qw, sw)
     _check(host_bf16_f64(c_plain), ref, f"plain {M}x{N}x{K}", mode, qa, sa, qw, sw)
+
+
+def test_gemm_on_side_stream_keeps_its_scratch(fgq_gpu):
+    # A call on a stream other than the current one allocates its output and
+    # split-K workspace from that stream's pool: memory allocated and written
+    # on the current stream right after the call cannot be the workspace the
+    # kernels are still writing.  Checked against the same call on the current
+    # stream, bit for bit.
+    import torch
+    rng = np.random.default_rng(3)
+    M, N, K = 64, 4096, 7168
+    qa = _int_codes((M, K), rng)
+    qw = _int_codes((N, K), rng)
+    sa = (2.0 ** rng.integers(-1, 2, (M, K // 128))).astype(np.float32)
+    sw = (2.0 ** rng.integers(-1, 2, (N // 128, K // 128))).astype(np.float32)
+    assert fgq_gpu.gemm_workspace_bytes(M, N, K) > 0      # the split-K path, which needs scratch
+    qa_d, qw_d, sa_d, sw_d = dev_u8(qa), dev_u8(qw), dev_f32(sa), dev_f32(sw)
+    want = fgq_gpu.gemm_fp8_blockscaled(qa_d, sa_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs, fills = [], []
+    for _ in range(4):
+        outs.append(fgq_gpu.gemm_fp8_blockscaled(qa_d, sa_d, qw_d, sw_d, stream=side))
+        # allocate and write on the current stream while the side stream runs
+        fills.append(torch.full((fgq_gpu.gemm_workspace_bytes(M, N, K) // 4,), 7.0, device="cuda"))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = want.view(torch.int16).cpu().numpy()
+    for o in outs:
+        assert np.array_equal(o.view(torch.int16).cpu().numpy(), ref)
+    for f in fills:
+        assert bool((f == 7.0).all())
