@@ -123,6 +123,11 @@ def load_library(path: str | None = None):
     global lib
     if lib is not None:
         return lib
+    # torch first: it brings its own HIP runtime, and libfgq must bind to that
+    # same runtime (same soname).  Loaded before torch, the library would pull
+    # in the system ROCm runtime and its launches would go to a second runtime
+    # that fails with "no device" once torch has set up its own.
+    _torch()
     path = path or library_path()
     if not os.path.exists(path):
         raise FgqError(-1, f"libfgq.so not found at {path}; build it with "

@@ -28,6 +28,11 @@ fgq_status_t from_hip(hipError_t e) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Before a call launches its kernels: clear an error that an unrelated
+// earlier HIP call left in this thread's error state, so that the
+// hipGetLastError() after the launch reports this call's launch only.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 // Common checks for a [rows, K] BF16 input / E4M3 + scale output pair;
 // s_align is the scale element's alignment (4 for binary32, 1 for E8M0).
 fgq_status_t check_act_io(const void* x, int64_t ldx, int64_t M, int64_t K, const void* q, int64_t ldq,
@@ -132,6 +137,7 @@ fgq_status_t fgq_quant_act_1x128(const void* x, int64_t ldx, int64_t M, int64_t 
                                  float* s, int64_t s_sm, int64_t s_skb, void* stream) {
   const fgq_status_t st = check_act_io(x, ldx, M, K, q, ldq, s, s_sm, s_skb);
   if (st != FGQ_OK || M == 0 || K == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_quant_act_1x128(static_cast<const uint16_t*>(x), ldx, M, K,
                                               static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb,
                                               as_stream(stream)));
@@ -142,6 +148,7 @@ fgq_status_t fgq_quant_w_128x128(const void* w, int64_t ldw, int64_t w_bs, int64
                                  int64_t s_skb, int64_t s_bs, void* stream) {
   const fgq_status_t st = check_quant_w(w, ldw, w_bs, B, N, K, q, ldq, q_bs, s, s_snb, s_skb, s_bs, 4);
   if (st != FGQ_OK || B == 0 || N == 0 || K == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_quant_w_128x128(static_cast<const uint16_t*>(w), ldw, w_bs, B, N, K,
                                               static_cast<uint8_t*>(q), ldq, q_bs, s, s_snb, s_skb, s_bs,
                                               as_stream(stream)));
@@ -152,6 +159,7 @@ fgq_status_t fgq_fused_rmsnorm_quant(const void* x, int64_t ldx, const void* gam
                                      int64_t s_skb, void* stream) {
   const fgq_status_t st = check_fused(x, ldx, gamma, M, K, q, ldq, s, s_sm, s_skb, 4);
   if (st != FGQ_OK || M == 0 || K == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_fused_rmsnorm_quant(static_cast<const uint16_t*>(x), ldx,
                                                   static_cast<const uint16_t*>(gamma), eps, M, K,
                                                   static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb,
@@ -172,6 +180,7 @@ fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* 
                                      mode == FGQ_GEMM_EXACT || mode == FGQ_GEMM_FP8_CORE, workspace,
                                      workspace_bytes, 4);
   if (st != FGQ_OK || M == 0 || N == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_gemm_fp8_blockscaled(
       static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, sw,
       sw_snb, sw_skb, static_cast<uint16_t*>(c), ldc, M, N, K, mode, workspace, workspace_bytes,
@@ -188,6 +197,7 @@ fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const
                                         offsets, E, total_rows, c, ldc, N, K,
                                         mode == FGQ_GEMM_EXACT || mode == FGQ_GEMM_FP8_CORE, 4);
   if (st != FGQ_OK || E == 0 || total_rows == 0 || N == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_grouped_gemm_fp8_blockscaled(
       static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, w_es,
       sw, sw_snb, sw_skb, sw_es, offsets, E, total_rows, static_cast<uint16_t*>(c), ldc, N, K, mode,
@@ -221,6 +231,7 @@ fgq_status_t fgq_gemm_bf16a_fp8_blockscaled(const void* a, int64_t lda, const vo
     if (workspace_bytes < need) return FGQ_ERR_SHAPE;
     if (!aligned(workspace, 256)) return FGQ_ERR_ALIGN;
   }
+  clear_stale_error();
   return from_hip(fgq::launch_gemm_bf16a_fp8_blockscaled(
       static_cast<const uint16_t*>(a), lda, static_cast<const uint8_t*>(qw), ldw, sw, sw_snb, sw_skb,
       static_cast<uint16_t*>(c), ldc, M, N, K, mode, static_cast<uint8_t*>(qa_out), ldq, sa_out, sa_sm, sa_skb,
@@ -231,6 +242,7 @@ fgq_status_t fgq_quant_act_1x128_e8m0(const void* x, int64_t ldx, int64_t M, int
                                       uint8_t* s, int64_t s_sm, int64_t s_skb, void* stream) {
   const fgq_status_t st = check_act_io(x, ldx, M, K, q, ldq, s, s_sm, s_skb, 1);
   if (st != FGQ_OK || M == 0 || K == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_quant_act_1x128_e8m0(static_cast<const uint16_t*>(x), ldx, M, K,
                                                    static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb,
                                                    as_stream(stream)));
@@ -241,6 +253,7 @@ fgq_status_t fgq_quant_w_128x128_e8m0(const void* w, int64_t ldw, int64_t w_bs, 
                                       int64_t s_skb, int64_t s_bs, void* stream) {
   const fgq_status_t st = check_quant_w(w, ldw, w_bs, B, N, K, q, ldq, q_bs, s, s_snb, s_skb, s_bs, 1);
   if (st != FGQ_OK || B == 0 || N == 0 || K == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_quant_w_128x128_e8m0(static_cast<const uint16_t*>(w), ldw, w_bs, B, N, K,
                                                    static_cast<uint8_t*>(q), ldq, q_bs, s, s_snb, s_skb, s_bs,
                                                    as_stream(stream)));
@@ -251,6 +264,7 @@ fgq_status_t fgq_fused_rmsnorm_quant_e8m0(const void* x, int64_t ldx, const void
                                           int64_t s_skb, void* stream) {
   const fgq_status_t st = check_fused(x, ldx, gamma, M, K, q, ldq, s, s_sm, s_skb, 1);
   if (st != FGQ_OK || M == 0 || K == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_fused_rmsnorm_quant_e8m0(static_cast<const uint16_t*>(x), ldx,
                                                        static_cast<const uint16_t*>(gamma), eps, M, K,
                                                        static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb,
@@ -265,6 +279,7 @@ fgq_status_t fgq_gemm_fp8_e8m0(const void* qa, int64_t lda, const uint8_t* sa, i
                                      accumulate == FGQ_E8M0_PROMOTE || accumulate == FGQ_E8M0_IN_CORE, workspace,
                                      workspace_bytes, 1);
   if (st != FGQ_OK || M == 0 || N == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_gemm_fp8_e8m0(static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb,
                                             static_cast<const uint8_t*>(qw), ldw, sw, sw_snb, sw_skb,
                                             static_cast<uint16_t*>(c), ldc, M, N, K,
@@ -281,6 +296,7 @@ fgq_status_t fgq_grouped_gemm_fp8_e8m0(const void* qa, int64_t lda, const uint8_
                                         offsets, E, total_rows, c, ldc, N, K,
                                         accumulate == FGQ_E8M0_PROMOTE || accumulate == FGQ_E8M0_IN_CORE, 1);
   if (st != FGQ_OK || E == 0 || total_rows == 0 || N == 0) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_grouped_gemm_fp8_e8m0(
       static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, w_es, sw,
       sw_snb, sw_skb, sw_es, offsets, E, total_rows, static_cast<uint16_t*>(c), ldc, N, K,
@@ -341,6 +357,7 @@ fgq_status_t fgq_quant_dispatch_1x128(const void* x, int64_t ldx, int64_t T, int
   const fgq_status_t st = check_dispatch(x, ldx, T, K, ids, topk, E, q, ldq, s, s_sm, s_skb, offsets, row_src, dest,
                                          workspace, workspace_bytes, 4);
   if (st != FGQ_OK) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_quant_dispatch_1x128(static_cast<const uint16_t*>(x), ldx, T, K, ids, topk, E,
                                                    static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb, offsets,
                                                    row_src, dest, workspace, as_stream(stream)));
@@ -353,6 +370,7 @@ fgq_status_t fgq_quant_dispatch_1x128_e8m0(const void* x, int64_t ldx, int64_t T
   const fgq_status_t st = check_dispatch(x, ldx, T, K, ids, topk, E, q, ldq, s, s_sm, s_skb, offsets, row_src, dest,
                                          workspace, workspace_bytes, 1);
   if (st != FGQ_OK) return st;
+  clear_stale_error();
   return from_hip(fgq::launch_quant_dispatch_1x128_e8m0(static_cast<const uint16_t*>(x), ldx, T, K, ids, topk, E,
                                                         static_cast<uint8_t*>(q), ldq, s, s_sm, s_skb, offsets,
                                                         row_src, dest, workspace, as_stream(stream)));
@@ -370,6 +388,7 @@ fgq_status_t fgq_debug_encode_e4m3(uint32_t start, int64_t n, void* out, void* s
   if (n < 0 || n > ((int64_t)1 << 32)) return FGQ_ERR_SHAPE;
   if (n == 0) return FGQ_OK;
   if (!out) return FGQ_ERR_NULL;
+  clear_stale_error();
   return from_hip(fgq::launch_debug_encode_e4m3(start, n, static_cast<uint8_t*>(out), as_stream(stream)));
 }
 
@@ -378,12 +397,14 @@ fgq_status_t fgq_debug_copy(const void* src, void* dst, int64_t bytes, void* str
   if (bytes == 0) return FGQ_OK;
   if (!src || !dst) return FGQ_ERR_NULL;
   if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0) return FGQ_ERR_ALIGN;
+  clear_stale_error();
   return from_hip(fgq::launch_debug_copy(src, dst, bytes, as_stream(stream)));
 }
 
 fgq_status_t fgq_debug_mfma_16x16x128(const void* a, const void* b, const float* cin, float* d, void* stream) {
   if (!a || !b || !cin || !d) return FGQ_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(cin, 4) || !aligned(d, 4)) return FGQ_ERR_ALIGN;
+  clear_stale_error();
   return from_hip(fgq::launch_debug_mfma(static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), cin, d,
                                          as_stream(stream)));
 }
@@ -392,6 +413,7 @@ fgq_status_t fgq_debug_mfma_e8m0_16x16x128(const void* a, const void* b, const u
                                            const float* cin, float* d, void* stream) {
   if (!a || !b || !sa || !sb || !cin || !d) return FGQ_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(cin, 4) || !aligned(d, 4)) return FGQ_ERR_ALIGN;
+  clear_stale_error();
   return from_hip(fgq::launch_debug_mfma_e8m0(static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b), sa, sb,
                                               cin, d, as_stream(stream)));
 }
@@ -403,6 +425,7 @@ fgq_status_t fgq_debug_mfma_loop(int32_t kind, int64_t iters, int64_t waves, uin
   if (waves == 0) return FGQ_OK;
   if (!out || !sink) return FGQ_ERR_NULL;
   if (!aligned(out, 8) || !aligned(sink, 4)) return FGQ_ERR_ALIGN;
+  clear_stale_error();
   return from_hip(fgq::launch_debug_mfma_loop(kind, iters, waves, out, sink, as_stream(stream)));
 }
 
