@@ -44,6 +44,7 @@ __all__ = [
     "quant_act_1x128_e8m0", "quant_w_128x128_e8m0", "fused_rmsnorm_quant_e8m0", "act_scales_e8m0",
     "gemm_fp8_e8m0", "grouped_gemm_fp8_e8m0", "debug_mfma_e8m0_16x16x128", "E8M0_PROMOTE", "E8M0_IN_CORE",
     "quant_dispatch_1x128_e8m0", "gemm_bf16a_fp8_blockscaled", "debug_mfma_loop", "MFMA_LOOP_FLOPS",
+    "gemm_fp8_blockscaled_noalloc",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +57,7 @@ E8M0_IN_CORE = 1     # E8M0 GEMMs: running sum kept in the matrix core (no promo
 
 STATUS = {
     0: "FGQ_OK", 1: "FGQ_ERR_NULL", 2: "FGQ_ERR_SHAPE", 3: "FGQ_ERR_ALIGN",
-    4: "FGQ_ERR_STRIDE", 5: "FGQ_ERR_UNSUPPORTED", 6: "FGQ_ERR_HIP",
+    4: "FGQ_ERR_STRIDE", 5: "FGQ_ERR_UNSUPPORTED", 6: "FGQ_ERR_HIP", 7: "FGQ_ERR_SCRATCH",
 }
 
 
@@ -104,6 +105,8 @@ _SIGNATURES = {
                                   _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _st, _vp],
     "fgq_debug_mfma_e8m0_16x16x128": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "fgq_debug_mfma_loop": [_st, _i64, _i64, _vp, _vp, _vp],
+    "fgq_gemm_fp8_blockscaled_noalloc": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
+                                         _i64, _i64, _i64, _st, _vp],
     "fgq_gemm_bf16a_fp8_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _st,
                                        _vp, _i64, _vp, _i64, _i64, _vp, ctypes.c_size_t, _vp],
     "fgq_quant_dispatch_1x128_e8m0": [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
@@ -388,6 +391,29 @@ def gemm_fp8_blockscaled(qa, sa, qw, sw, out=None, workspace=None, mode=GEMM_EXA
     ``mode``: GEMM_EXACT (default) or GEMM_FP8_CORE."""
     load_library()
     return _gemm(lib.fgq_gemm_fp8_blockscaled, _torch().float32, qa, sa, qw, sw, out, workspace, mode, stream)
+
+
+def gemm_fp8_blockscaled_noalloc(qa, sa, qw, sw, out, mode=GEMM_EXACT, stream=None):
+    """gemm_fp8_blockscaled through the library's no-allocation entry point:
+    the call uses the library's own device scratch and allocates nothing, so
+    ``out`` (bfloat16 [M, N]) must be given.  Calls that can overlap on one GPU
+    share that scratch and must be serialised by the caller."""
+    torch = _torch()
+    load_library()
+    qa, qw = _codes(qa), _codes(qw)
+    _need(qa, torch.uint8, "qa")
+    _need(qw, torch.uint8, "qw")
+    _need_scales(sa, "sa")
+    _need_scales(sw, "sw")
+    _need(out, torch.bfloat16, "out")
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("qa, qw and out disagree on M, N or K")
+    _check(lib.fgq_gemm_fp8_blockscaled_noalloc(
+        _ptr(qa), qa.stride(0), _ptr(sa), sa.stride(0), sa.stride(1), _ptr(qw), qw.stride(0), _ptr(sw),
+        sw.stride(0), sw.stride(1), _ptr(out), out.stride(0), M, N, K, int(mode), _stream(stream)))
+    return out
 
 
 def gemm_fp8_e8m0(qa, sa, qw, sw, out=None, workspace=None, accumulate=E8M0_PROMOTE, stream=None):

@@ -187,6 +187,28 @@ fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* 
       as_stream(stream)));
 }
 
+fgq_status_t fgq_gemm_fp8_blockscaled_noalloc(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                                              int64_t sa_skb, const void* qw, int64_t ldw, const float* sw,
+                                              int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc, int64_t M,
+                                              int64_t N, int64_t K, int32_t mode, void* stream) {
+  // the same checks as fgq_gemm_fp8_blockscaled, with the library's scratch
+  // in place of a workspace (its address is checked below, not here)
+  const size_t room = fgq::noalloc_scratch_bytes();
+  if (M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0 && fgq::gemm_workspace_required(M, N, K) > room)
+    return FGQ_ERR_SCRATCH;
+  const void* const placeholder = reinterpret_cast<const void*>((uintptr_t)256);  // aligned, non-null
+  const fgq_status_t st = check_gemm(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K,
+                                     mode == FGQ_GEMM_EXACT || mode == FGQ_GEMM_FP8_CORE, placeholder, room, 4);
+  if (st != FGQ_OK || M == 0 || N == 0) return st;
+  void* ws = nullptr;
+  const fgq_status_t sst = from_hip(fgq::noalloc_scratch(&ws));
+  if (sst != FGQ_OK) return sst;
+  clear_stale_error();
+  return from_hip(fgq::launch_gemm_fp8_blockscaled(
+      static_cast<const uint8_t*>(qa), lda, sa, sa_sm, sa_skb, static_cast<const uint8_t*>(qw), ldw, sw,
+      sw_snb, sw_skb, static_cast<uint16_t*>(c), ldc, M, N, K, mode, ws, room, as_stream(stream)));
+}
+
 fgq_status_t fgq_grouped_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
                                               int64_t sa_skb, const void* qw, int64_t ldw, int64_t w_es,
                                               const float* sw, int64_t sw_snb, int64_t sw_skb,
@@ -312,6 +334,7 @@ const char* fgq_status_string(fgq_status_t status) {
     case FGQ_ERR_STRIDE: return "leading dimension or stride too small or misaligned";
     case FGQ_ERR_UNSUPPORTED: return "size not supported (K and N must be multiples of 128)";
     case FGQ_ERR_HIP: return "HIP launch failed (see fgq_last_hip_error)";
+    case FGQ_ERR_SCRATCH: return "the product needs more scratch than the no-allocation entry point holds (48 MiB)";
     default: return "unknown status";
   }
 }

@@ -25,6 +25,11 @@ hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const flo
                                        int64_t M, int64_t N, int64_t K, int mode, void* workspace,
                                        size_t workspace_bytes, hipStream_t st);
 
+// The no-allocation variant's device scratch: its size, and this device's
+// address of it (resolved once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 // recommended size (lets large products split their last round) and the
 // size the call requires (split-K of small M)
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -51,6 +51,7 @@
 //     pages report for H800.
 //     Scale bytes travel in the same 4-byte DMA slots as binary32 scales
 //     (the aligned word holding the byte) and are read back as single bytes.
+#include <mutex>
 #include <type_traits>
 
 #include "fgq_device.h"
@@ -1187,6 +1188,42 @@ hipError_t launch_gemm_fp8_blockscaled(const uint8_t* qa, int64_t lda, const flo
                             workspace_bytes, st);
   return gemm_dispatch<0>(qa, lda, sa, sa_sm, sa_skb, qw, ldw, sw, sw_snb, sw_skb, c, ldc, M, N, K, workspace,
                             workspace_bytes, st);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate device memory (code under graph
+// capture, allocation-free serving loops): fgq_gemm_fp8_blockscaled_noalloc
+// runs the products of fgq_gemm_fp8_blockscaled with this file-scope array as
+// their workspace.  Every GPU holds its own copy at its own address, resolved
+// once per device with hipGetSymbolAddress; host code never passes the
+// array's name itself to a kernel (on the host it is only a stand-in).
+// Nothing in it needs to start at zero: every call writes the partial sums
+// it reads back.  Calls that overlap on one GPU share it and race.  48 MiB
+// holds the split-K partial sums of every small-M shape (at most 256 tiles of
+// 64 x 128, split at most 512 / tiles ways: at most 16.8 MB) and the
+// last-round split of an 8192 x 18432 product (47.2 MB).
+constexpr size_t kNoAllocScratchBytes = (size_t)48 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_fp8_e8m0(const uint8_t* qa, int64_t lda, const uint8_t* sa, int64_t sa_sm, int64_t sa_skb,

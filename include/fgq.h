@@ -54,10 +54,11 @@ enum {
   FGQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
   FGQ_ERR_STRIDE = 4,      /* a leading dimension / stride is too small or misaligned */
   FGQ_ERR_UNSUPPORTED = 5, /* sizes outside what the kernels support (e.g. K % 128 != 0) */
-  FGQ_ERR_HIP = 6          /* a HIP launch failed; see fgq_last_hip_error() */
+  FGQ_ERR_HIP = 6,         /* a HIP launch failed; see fgq_last_hip_error() */
+  FGQ_ERR_SCRATCH = 7      /* fgq_gemm_fp8_blockscaled_noalloc: the product needs more scratch than it holds */
 };
 
-#define FGQ_ABI_VERSION 5
+#define FGQ_ABI_VERSION 6
 
 /*
  * fgq_quant_act_1x128 -- online activation quantisation, one scale per
@@ -181,6 +182,30 @@ fgq_status_t fgq_gemm_fp8_blockscaled(const void* qa, int64_t lda, const float* 
                                       int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc,
                                       int64_t M, int64_t N, int64_t K, int32_t mode, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * fgq_gemm_fp8_blockscaled_noalloc -- fgq_gemm_fp8_blockscaled for callers
+ * that cannot allocate device memory (code under HIP graph capture,
+ * allocation-free serving loops, harnesses that forbid hipMalloc): the same
+ * product, the same kernels and the same results as fgq_gemm_fp8_blockscaled
+ * given a 48 MiB workspace, with a scratch array inside the library (48 MiB
+ * per GPU, allocated when the library's code is loaded on that GPU and held
+ * until the process ends) in place of the workspace.  The call allocates
+ * nothing and calls no allocating routine; the caller still passes every
+ * input and output.
+ *   Arguments as in fgq_gemm_fp8_blockscaled, without workspace.
+ *   A product whose required workspace (the split along K of small M, at
+ *   most 16.8 MB for any shape the ABI accepts) exceeded 48 MiB would
+ *   return FGQ_ERR_SCRATCH; a large product splits its last round of tiles
+ *   only when their partial sums fit (8192 x 18432 products do).
+ *   Every call on one GPU uses that GPU's one scratch array: calls that can
+ *   overlap on the same GPU (different streams or threads) race and must
+ *   be serialised by the caller.
+ */
+fgq_status_t fgq_gemm_fp8_blockscaled_noalloc(const void* qa, int64_t lda, const float* sa, int64_t sa_sm,
+                                              int64_t sa_skb, const void* qw, int64_t ldw, const float* sw,
+                                              int64_t sw_snb, int64_t sw_skb, void* c, int64_t ldc, int64_t M,
+                                              int64_t N, int64_t K, int32_t mode, void* stream);
 
 /* Bytes of workspace for fgq_gemm_fp8_blockscaled (and its E8M0 variant) at
  * this shape: what small M requires, and what lets a large product split its

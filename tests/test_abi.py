@@ -45,8 +45,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fgq_abi_version() == 5
-    for code in range(7):
+    assert lib.fgq_abi_version() == 6
+    for code in range(8):
         assert lib.fgq_status_string(code)
     assert lib.fgq_status_string(99) == b"unknown status"
     assert lib.fgq_last_hip_error() == 0
@@ -330,3 +330,21 @@ def test_gemm_bf16a_validation(lib):
     need = lib.fgq_gemm_workspace_bytes(64, 18432, 7168)
     assert gemm16(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168) == NULL      # no workspace
     assert gemm16(lib, M=64, N=18432, K=7168, ldc=18432, lda=7168, ldw=7168, ws=P, ws_bytes=need - 1) == SHAPE
+
+
+def test_gemm_noalloc_validation(lib):
+    na = lib.fgq_gemm_fp8_blockscaled_noalloc
+
+    def call(qa=P, lda=256, sa=S, qw=Q, ldw=256, sw=S, c=Q, ldc=256, M=4, N=256, K=256, mode=0):
+        return na(qa, lda, sa, 2, 1, qw, ldw, sw, 2, 1, c, ldc, M, N, K, mode, None)
+    assert call(M=-1) == SHAPE
+    assert call(mode=2) == UNSUP
+    assert call(N=100) == UNSUP
+    assert call(K=0) == UNSUP
+    assert call(M=0) == OK
+    assert call(N=0) == OK
+    assert call(qa=0) == NULL
+    assert call(c=Q + 2) == ALIGN
+    assert call(lda=128) == STRIDE
+    assert call(lda=(1 << 24) + 16) == UNSUP
+    assert lib.fgq_status_string(7)
