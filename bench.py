@@ -96,6 +96,13 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+class NoTimer:
+    """Runs the launches and records nothing (device warm-up)."""
+
+    def run(self, name, fn):
+        return fn()
+
+
 class Timer:
     """HIP events around launches on the current stream, summed per name."""
 
@@ -450,26 +457,28 @@ def main():
     print(f"[bench] building {args.workload} inputs", file=sys.stderr, flush=True)
     d, sets, flops, quant_bytes, shape = build_sets(args)
     step = make_step(args, fgq, d, len(sets), gemm_mode(fgq, args.mode))
-    warm = Timer()
     # Device warm-up, untimed: the chip takes tens of milliseconds of
-    # sustained load to settle its clocks (a 2 ms prefill GEMM ran 2.1-2.35 ms
-    # in its first calls and 1.76 ms after twenty), so the step is repeated
-    # for PREWARM_S of wall time before the counted warm-up steps.
+    # sustained load to settle its clocks (after an idle gap of 25 ms a 1.75 ms
+    # prefill GEMM ran 2.1-2.37 ms and needed about fifteen calls to settle),
+    # so the step is repeated for PREWARM_S of wall time before the counted
+    # warm-up steps, and the timed steps follow the warm-up steps with no host
+    # work in between beyond one synchronisation.
+    warm, timer = Timer(), Timer()
+    # A 256-byte device copy on each side of the timed region, outside the
+    # events: in a kernel trace of this run, the dispatches between the two
+    # copies are exactly the timed steps.
+    mark = torch.zeros(512, dtype=torch.uint8, device="cuda")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_pre, t_pre = 0, time.perf_counter()
     while time.perf_counter() - t_pre < PREWARM_S:
         for _ in range(4):
-            step(n_pre % len(sets), sets[n_pre % len(sets)], warm)
+            step(n_pre % len(sets), sets[n_pre % len(sets)], NoTimer())
             n_pre += 1
         torch.cuda.synchronize()
-    warm = Timer()
     for i in range(args.warmup):
         step(i % len(sets), sets[i % len(sets)], warm)
+    fgq.debug_copy(mark[:256], mark[256:])
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({n_pre} device warm-up steps, {args.warmup} counted warm-up steps, "
-          f"{len(sets)} input sets)", file=sys.stderr, flush=True)
-    timer = Timer()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
@@ -477,6 +486,10 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    fgq.debug_copy(mark[:256], mark[256:])
+    torch.cuda.synchronize()
+    print(f"[bench] {n_pre} device warm-up steps, {args.warmup} counted warm-up steps, {len(sets)} input sets",
+          file=sys.stderr, flush=True)
     ms_step = start.elapsed_time(end) / args.steps
     kern = timer.avg_ms()
     spread = timer.spread_ms()
@@ -514,6 +527,7 @@ def main():
                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
                     "peak_note": "dense FP8 MFMA peak (the metric's); the exact mode's products run on the "
                                  "FP16 matrix cores" if args.mode == "exact" else "dense FP8 MFMA peak",
+                    "algorithmic_flops": flops,
                     "frac_contraction_dtype_peak": achieved / dtype_peak,
                     "contraction_dtype": "fp16" if args.mode == "exact" else "fp8",
                     "traffic": traffic}

@@ -2,15 +2,31 @@
 
     python -m fine_grained_fp8_quant_amd.profile_summary <out_dir> <workload>[:e8m0] [...]
 
-<out_dir> holds, per workload, the output of the two commands printed in
-each summary (a kernel trace of bench.py, and FETCH_SIZE / WRITE_SIZE
-counter passes of profile_workload.py).  Writes profiles/<workload>_kernels.md
-(<workload>_e8m0_kernels.md for the power-of-two scale variant) and updates
-profiles/traffic.json with HBM bytes per launch.
+<out_dir> holds, per workload, the output of the commands printed in each
+summary: a kernel trace of bench.py (with bench.py's own JSON line saved
+beside it), FETCH_SIZE / WRITE_SIZE counter passes of profile_workload.py
+and, for the GEMM-bound workloads, three passes of utilisation counters.
+Writes profiles/<workload>_kernels.md (<workload>_e8m0_kernels.md for the
+power-of-two scale variant) and updates profiles/traffic.json with HBM bytes
+per launch.
+
+Timed steps: bench.py launches a 256-byte device copy (fgq_debug_copy) just
+before and just after its timed region.  The per-call table averages only the
+dispatches between those two copies, so it covers the same calls as the
+HIP-event times of the bench line saved with the trace.
 
 Traffic calibration: the counter passes also run a 1 GiB device copy
 (fgq_debug_copy).  Its FETCH_SIZE and WRITE_SIZE against the known 1 GiB
 read and 1 GiB written give the factors applied to every kernel.
+
+Utilisation counters (per dispatch, then averaged per kernel):
+  clock        GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration (launches of 200 us
+               or more only)
+  MFMA busy    SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)
+  co-issue     SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES
+  waiting      SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave-cycles waiting on anything)
+  LDS conflict SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+  L2 hit       TCC_HIT / (TCC_HIT + TCC_MISS)
 """
 from __future__ import annotations
 
@@ -28,10 +44,22 @@ SOURCES = {"gemm": "fine_grained_fp8_quant_amd/csrc/gemm.hip", "quant": "fine_gr
            "dispatch": "fine_grained_fp8_quant_amd/csrc/dispatch.hip"}
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace/{tag} -o trace -- "
-             "python -u bench.py --workload {w} --scales {sc} --steps 5 --warmup 2 --no-cpu-baseline")
+             "python -u bench.py --workload {w} --scales {sc} --steps 20 --warmup 5 --no-cpu-baseline "
+             "> <out>/trace/{tag}/bench.json")
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{tag}/{c} -o pmc -- "
            "python -u -m fine_grained_fp8_quant_amd.profile_workload --workload {w} --scales {sc}")
+UTIL_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc/{tag}/{p} -o pmc -- "
+            "python -u -m fine_grained_fp8_quant_amd.profile_workload --workload {w} --scales {sc}")
 MODE_NAMES = {"0": "exact", "1": "fp8core", "2": "promote", "3": "incore"}
+# utilisation counter passes: each fits one rocprofv3 run (at most 8 SQ,
+# 4 TCC and 2 GRBM counters)
+UTIL_PASSES = {
+    "util": "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
+            "SQ_INSTS_LDS",
+    "stall": "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE",
+    "l2": "GRBM_GUI_ACTIVE TCC_HIT_sum TCC_MISS_sum",
+}
+N_XCD, N_SIMD = 8, 1024
 
 
 def sha(rel):
@@ -103,12 +131,82 @@ def read_pmc(path):
     return [(k, v) for _, k, v in out]
 
 
+def read_trace_timed(path):
+    """(kernel, duration us) of every dispatch between the first two marker
+    copies (k_debug_copy) of a kernel trace, in dispatch order; None when the
+    trace holds fewer than two markers."""
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Dispatch_Id"]), short(r["Kernel_Name"]),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    marks = [i for i, (_, k, _) in enumerate(rows) if k.startswith("k_debug_copy")]
+    if len(marks) < 2:
+        return None
+    return [(k, us) for _, k, us in rows[marks[0] + 1:marks[1]]]
+
+
+def read_counters(path):
+    """{dispatch id: (kernel, duration ns, {counter: value})} of one --pmc pass."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            if d not in out:
+                out[d] = (short(r["Kernel_Name"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {})
+            out[d][2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def util_metrics(passes):
+    """Per-kernel averages of the utilisation ratios over the dispatches of
+    the counter passes ({pass name: read_counters output})."""
+    per = defaultdict(lambda: defaultdict(list))
+    for name, disp in passes.items():
+        for k, dur, c in disp.values():
+            if k.startswith("k_debug_copy") or dur <= 0 or not c.get("GRBM_GUI_ACTIVE"):
+                continue
+            cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+            m = per[k]
+            if dur >= 200_000:
+                # the counter also runs through the launch's set-up and
+                # drain, which only long launches make negligible
+                m["clock GHz"].append(cyc / dur)
+            if name == "util":
+                busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+                m["MFMA busy"].append(busy / (N_SIMD * cyc))
+                if busy:
+                    m["co-issue / MFMA busy"].append(c["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy)
+                if c["SQ_INSTS_MFMA"]:
+                    m["VALU inst / MFMA inst"].append(c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"])
+                    m["LDS inst / MFMA inst"].append(c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"])
+            elif name == "stall":
+                if c["SQ_WAVE_CYCLES"]:
+                    m["waiting"].append(c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"])
+                    m["waiting to issue"].append(c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"])
+                if c["SQ_LDS_IDX_ACTIVE"]:
+                    m["LDS conflict"].append(c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"])
+            elif name == "l2":
+                tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+                if tot:
+                    m["L2 hit"].append(c["TCC_HIT_sum"] / tot)
+    return {k: {n: sum(v) / len(v) for n, v in m.items()} for k, m in per.items()}
+
+
 def summarise(out_dir, spec, traffic):
     w, _, sc = spec.partition(":")
     sc = sc or "f32"
     e8 = sc == "e8m0"
     tag = w + ("_e8m0" if e8 else "")
-    stats = read_stats(os.path.join(out_dir, "trace", tag, "trace_kernel_stats.csv"))
+    tdir = os.path.join(out_dir, "trace", tag)
+    stats = read_stats(os.path.join(tdir, "trace_kernel_stats.csv"))
+    timed = read_trace_timed(os.path.join(tdir, "trace_kernel_trace.csv"))
+    bench = None
+    if os.path.exists(os.path.join(tdir, "bench.json")):
+        with open(os.path.join(tdir, "bench.json")) as f:
+            lines = [ln for ln in f if ln.startswith("{")]
+        bench = json.loads(lines[-1]) if lines else None
     fetch = read_pmc(os.path.join(out_dir, "pmc", tag, "FETCH_SIZE", "pmc_counter_collection.csv"))
     write = read_pmc(os.path.join(out_dir, "pmc", tag, "WRITE_SIZE", "pmc_counter_collection.csv"))
     gib_kib = 1024 * 1024
@@ -121,30 +219,64 @@ def summarise(out_dir, spec, traffic):
     for k, v in write:
         per_kernel[k][1].append(v * w_factor * 1024)
     title = w + (" with power-of-two (E8M0) scales" if e8 else "")
+    util_passes = {p: os.path.join(out_dir, "pmc", tag, p, "pmc_counter_collection.csv") for p in UTIL_PASSES}
+    util_passes = {p: path for p, path in util_passes.items() if os.path.exists(path)}
+    cmds = ["    " + TRACE_CMD.format(w=w, sc=sc, tag=tag),
+            "    " + PMC_CMD.format(w=w, sc=sc, tag=tag, c="FETCH_SIZE"),
+            "    " + PMC_CMD.format(w=w, sc=sc, tag=tag, c="WRITE_SIZE")]
+    cmds += ["    " + UTIL_CMD.format(w=w, sc=sc, tag=tag, p=p, c=UTIL_PASSES[p]) for p in util_passes]
     lines = [f"# {title}: kernel durations and HBM traffic (one MI355X)", "",
-             "Commands (from the repository root; `<out>` is any scratch directory):", "",
-             "    " + TRACE_CMD.format(w=w, sc=sc, tag=tag), "    " + PMC_CMD.format(w=w, sc=sc, tag=tag, c="FETCH_SIZE"),
-             "    " + PMC_CMD.format(w=w, sc=sc, tag=tag, c="WRITE_SIZE"),
-             "    python -m fine_grained_fp8_quant_amd.profile_summary <out> " + spec, "",
-             "## Kernel trace (`--kernel-trace --stats`; includes warm-up calls)", "",
-             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
-    for name, calls, avg, mn, mx, pct in stats:
-        lines.append(f"| {name} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f} |")
+             "Commands (from the repository root; `<out>` is any scratch directory):", "", *cmds,
+             "    python -m fine_grained_fp8_quant_amd.profile_summary <out> " + spec, ""]
     # one call of the C ABI can launch several kernels (split-K and its
     # reduction; the dense last-round split and its reduction): their
     # average durations add up to the call
-    per_call = defaultdict(float)
+    def per_call_table(rows):
+        per_call = defaultdict(float)
+        for name, avg in rows:
+            api, mode = api_of(name, e8)
+            if not api:
+                continue
+            modes = [mode] if mode or "gemm" not in api else (["promote", "incore"] if e8 else ["exact", "fp8core"])
+            for md in modes:
+                per_call[api + (f"[{md}]" if md else "")] += avg
+        return per_call
+
+    if timed is not None:
+        tk = defaultdict(list)
+        for k, us in timed:
+            tk[k].append(us)
+        lines += ["## Timed steps only (the dispatches between the two marker copies)", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for k, v in sorted(tk.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+        per_call = per_call_table([(k, sum(v) / len(v)) for k, v in tk.items()])
+        lines += ["", "Per call over the timed steps (sum of the average durations of the call's kernels):", "",
+                  "| call | avg us |", "|---|---|"]
+        for key in sorted(per_call):
+            lines.append(f"| {key} | {per_call[key]:.1f} |")
+        if bench:
+            rf = bench["roofline"]
+            gk = rf["kernel"]
+            mode = bench.get("gemm_mode")
+            gemm_api = [key for key in per_call if key.startswith(("gemm", "grouped")) and
+                        (key.endswith(f"[{mode}]") or "[" not in key)]
+            ms_ev = bench["kernels"][gk]["ms"]
+            lines += ["", "## The bench line of the traced run", "",
+                      f"    roofline: bound {rf['bound']}, achieved {rf['achieved']:.1f} {rf['unit']}, "
+                      f"peak {rf['peak']}, frac {rf['frac']:.4f}",
+                      f"    {gk}: {ms_ev * 1e3:.1f} us per call (HIP events); "
+                      f"ms_per_step {bench['ms_per_step']:.4f}", ""]
+            if gemm_api:
+                us_tr = per_call[gemm_api[0]]
+                frac_tr = rf["frac"] * (ms_ev * 1e3) / us_tr
+                lines += [f"Recomputed from the trace: {gemm_api[0]} {us_tr:.1f} us per call, so frac = "
+                          f"{rf['frac']:.4f} x {ms_ev * 1e3:.1f} / {us_tr:.1f} = {frac_tr:.4f} "
+                          f"({(frac_tr / rf['frac'] - 1) * 100:+.1f}% against the line).", ""]
+    lines += ["## Kernel trace of the whole run (`--kernel-trace --stats`; includes warm-up calls)", "",
+              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
-        api, mode = api_of(name, e8)
-        if not api:
-            continue
-        modes = [mode] if mode or "gemm" not in api else (["promote", "incore"] if e8 else ["exact", "fp8core"])
-        for md in modes:
-            per_call[api + (f"[{md}]" if md else "")] += avg
-    lines += ["", "Per call (sum of the average durations of the call's kernels):", "",
-              "| call | avg us |", "|---|---|"]
-    for key in sorted(per_call):
-        lines.append(f"| {key} | {per_call[key]:.1f} |")
+        lines.append(f"| {name} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f} |")
     lines += ["", "## HBM traffic per launch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
               f"Calibration from the 1 GiB copy in the same runs: FETCH_SIZE x{f_factor:.3f}, "
               f"WRITE_SIZE x{w_factor:.3f}.", "",
@@ -167,6 +299,18 @@ def summarise(out_dir, spec, traffic):
                 sums[key][2] = sha(SOURCES["gemm" if "gemm" in api else ("dispatch" if "dispatch" in api else "quant")])
     for key, (rd, wr, src) in sums.items():
         traffic[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr, "source_sha": src}
+    if util_passes:
+        um = util_metrics({p: read_counters(path) for p, path in util_passes.items()})
+        names = ["clock GHz", "MFMA busy", "co-issue / MFMA busy", "VALU inst / MFMA inst", "LDS inst / MFMA inst",
+                 "waiting", "waiting to issue", "LDS conflict", "L2 hit"]
+        lines += ["", "## Utilisation counters per launch (averaged over the launches of each kernel)", "",
+                  "| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        for k in sorted(um):
+            vals = []
+            for n in names:
+                v = um[k].get(n)
+                vals.append("-" if v is None else (f"{v:.2f}" if n.endswith(("GHz", "inst")) else f"{v * 100:.1f}%"))
+            lines.append(f"| {k} | " + " | ".join(vals) + " |")
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{tag}_kernels.md"), "w") as f:
         f.write("\n".join(lines) + "\n")

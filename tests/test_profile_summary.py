@@ -28,3 +28,48 @@ def test_gemm_kernels_and_their_reductions():
     assert api_of("k_tail_reduce<TileCfg<256, 256, 2, 4, 2, false> >", True) == ("gemm_fp8_e8m0", "promote")
     assert api_of("k_tail_reduce<TileCfg<256, 256, 4, 4, 2, false> >", True) == ("gemm_fp8_e8m0", "incore")
     assert api_of("__amd_rocclr_copyBuffer", False) == (None, None)
+
+
+def _write_csv(path, header, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_timed_dispatches_are_those_between_the_markers(tmp_path):
+    from fine_grained_fp8_quant_amd.profile_summary import read_trace_timed
+    hdr = ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows = [[1, "void fgq::k_quant_act_1x128<fgq::ScaleF32>(int)", 0, 5000],
+            [2, "void fgq::k_debug_copy(int)", 6000, 7000],
+            [4, "void fgq::k_quant_act_1x128<fgq::ScaleF32>(int)", 9000, 12000],
+            [3, "void fgq::k_quant_w_128x128<fgq::ScaleF32, false>(int)", 8000, 8500],
+            [5, "void fgq::k_debug_copy(int)", 13000, 14000],
+            [6, "void fgq::k_quant_act_1x128<fgq::ScaleF32>(int)", 15000, 99000]]
+    _write_csv(tmp_path / "t.csv", hdr, rows)
+    got = read_trace_timed(tmp_path / "t.csv")
+    assert got == [("k_quant_w_128x128<ScaleF32, false>", 0.5), ("k_quant_act_1x128<ScaleF32>", 3.0)]
+    _write_csv(tmp_path / "u.csv", hdr, rows[:2])
+    assert read_trace_timed(tmp_path / "u.csv") is None
+
+
+def test_utilisation_ratios(tmp_path):
+    from fine_grained_fp8_quant_amd.profile_summary import read_counters, util_metrics
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    k = "void fgq::k_gemm_fp8_bs<fgq::TileCfg<192, 256, 2, 4, 2, false>, 0>(int)"
+    # 1 ms at 2 GHz on every XCD: 2e6 cycles each, 1.6e7 summed
+    util = [[7, k, "GRBM_GUI_ACTIVE", 1.6e7, 0, 1_000_000], [7, k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1e6, 0, 1_000_000],
+            [7, k, "SQ_VALU_MFMA_COEXEC_CYCLES", 256 * 1e6, 0, 1_000_000], [7, k, "SQ_INSTS_MFMA", 100, 0, 1_000_000],
+            [7, k, "SQ_INSTS_VALU", 250, 0, 1_000_000], [7, k, "SQ_INSTS_LDS", 30, 0, 1_000_000]]
+    l2 = [[7, k, "GRBM_GUI_ACTIVE", 1.6e7, 0, 1_000_000], [7, k, "TCC_HIT_sum", 3, 0, 1_000_000],
+          [7, k, "TCC_MISS_sum", 1, 0, 1_000_000]]
+    _write_csv(tmp_path / "util.csv", hdr, util)
+    _write_csv(tmp_path / "l2.csv", hdr, l2)
+    m = util_metrics({"util": read_counters(tmp_path / "util.csv"), "l2": read_counters(tmp_path / "l2.csv")})
+    got = m["k_gemm_fp8_bs[192x256,exact]"]
+    assert abs(got["clock GHz"] - 2.0) < 1e-12
+    assert abs(got["MFMA busy"] - 0.5) < 1e-12
+    assert abs(got["co-issue / MFMA busy"] - 0.25) < 1e-12
+    assert abs(got["VALU inst / MFMA inst"] - 2.5) < 1e-12
+    assert abs(got["L2 hit"] - 0.75) < 1e-12
