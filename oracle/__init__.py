@@ -33,6 +33,12 @@ Precision: quantisation is exact-spec IEEE binary32 (NumPy float32 on x86,
 no flush-to-zero), so it has one correct answer per input.  The GEMM is its
 definition evaluated in float64.
 
+The per-tensor-scaling ablation (``oracle.ablation``, run as ``python -m
+oracle.ablation``) quantises the same operands with one scale per tensor and
+reports both products' errors against the unquantised BF16 product; it is a
+reported diagnostic of the pages' outlier claim [P2 paragraph 3, P4
+paragraph 3], not a gate.
+
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, exhaustive enumeration or library
 routines.  The summation order of the fused RMSNorm
