@@ -183,7 +183,7 @@ __device__ __forceinline__ int lds_col(int c, int r) { return c ^ (((r >> 3) & 1
 // scales applied by the unit (MODE 2 promote, MODE 3 in-core).  Lane
 // (l16, lgrp) feeds row l16 of a sub-tile with code bytes 32 lgrp ...
 // 32 lgrp + 31 of the chunk.
-template <class C, int MODE, bool LATE = true>
+template <class C, int MODE, bool LATE = true, bool IL = true>
 struct Engine16 {
   v4f acc[C::TM][C::TN];
   int wm, wn, l16, lgrp;
@@ -372,6 +372,102 @@ struct Engine16 {
     }
   }
 
+  // One full-height row of the exact path (four K = 32 steps into the
+  // chunk sums tc) with the instruction order fixed in the source: each
+  // matrix operation is followed by two vector instructions, fenced so the
+  // compiler keeps them together.  The vector work is the conversions of
+  // the next K step's A codes, the previous row's promotion arow += tp * sp,
+  // and this row's scale products sc = sa4 * swv.  Both waves of a SIMD run
+  // this program in step behind the chunk barrier: left to itself the
+  // compiler emits matrix operations and vector work in bursts of eight or
+  // more, and the two waves' bursts collide instead of overlapping.
+  // (four column sub-tiles: TN = 4)
+  __device__ __forceinline__ void row_interleaved(v4f (&tc)[C::TN], const uint4& lo, const uint4& hi,
+                                                  v4f (&arow)[C::TN], const v4f (&tp)[C::TN], const v4f& sp,
+                                                  v4f& sc, const v4f& sa4, float swv) {
+    const uint32_t aw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    v2h ap[4][4];
+    // pair p of K step ks: the two conversions of word 2 ks + p
+    auto cvt2 = [&](int ks, int p) {
+      ap[ks][2 * p] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(aw[2 * ks + p], 1.0f, false);
+      ap[ks][2 * p + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(aw[2 * ks + p], 1.0f, true);
+    };
+    // promotion multiply-adds 2 k and 2 k + 1 (sub-tile k / 2, elements 2 (k % 2) ..)
+    auto fma2 = [&](int k) {
+      const int ni = k >> 1, e = (k & 1) * 2;
+      arow[ni][e] = __builtin_fmaf(tp[ni][e], sp[e], arow[ni][e]);
+      arow[ni][e + 1] = __builtin_fmaf(tp[ni][e + 1], sp[e + 1], arow[ni][e + 1]);
+    };
+    cvt2(0, 0);
+    cvt2(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ks = j >> 2, ni = j & 3;
+      const v8h a = (v8h){ap[ks][0][0], ap[ks][0][1], ap[ks][1][0], ap[ks][1][1],
+                          ap[ks][2][0], ap[ks][2][1], ap[ks][3][0], ap[ks][3][1]};
+      tc[ni] = mfma_16x16x32_f16(a, bhm[ni][ks], ks == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : tc[ni]);
+      // fillers: after operations 0, 1 of steps 0-2 the next step's
+      // conversions; after 2, 3 of steps 0-2 and 0, 1 of step 3 the
+      // promotion; after the last two the scale products
+      if (ks < 3 && ni < 2) {
+        cvt2(ks + 1, ni);
+      } else if (j < 14) {
+        fma2(ks < 3 ? 2 * ks + (ni - 2) : 6 + ni);
+      } else {
+        const int e = (j - 14) * 2;
+        sc[e] = sa4[e] * swv;
+        sc[e + 1] = sa4[e + 1] * swv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // The previous chunk's deferred last row (A codes pa_lo / pa_hi, old FP16
+  // B fragments in bhm) into the chunk sums tp, in the fixed order of
+  // row_interleaved; the fillers are the row's remaining A conversions and
+  // the new chunk's B conversions from blo / bhi: fragment (ni, ks) is
+  // replaced two matrix operations after the one that read it (the last two
+  // after the row).
+  // Row 0's A codes and scales (alo, ahi, sa4) are requested halfway
+  // through, when half the B words are converted and their registers free.
+  __device__ __forceinline__ void deferred_interleaved(v4f (&tp)[C::TN], const uint4 (&blo)[C::TN],
+                                                       const uint4 (&bhi)[C::TN], const uint8_t* base, uint4& alo,
+                                                       uint4& ahi, v4f& sa4) {
+    const uint32_t aw[8] = {pa_lo.x, pa_lo.y, pa_lo.z, pa_lo.w, pa_hi.x, pa_hi.y, pa_hi.z, pa_hi.w};
+    v2h ap[4][4];
+    auto cvt1 = [&](int ks, int q) {
+      if (q & 1) ap[ks][q] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(aw[2 * ks + (q >> 1)], 1.0f, true);
+      else ap[ks][q] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(aw[2 * ks + (q >> 1)], 1.0f, false);
+    };
+    auto newb = [&](int j) {
+      const int ks = j >> 2, ni = j & 3;
+      const uint32_t w0 = ks == 0 ? blo[ni].x : ks == 1 ? blo[ni].z : ks == 2 ? bhi[ni].x : bhi[ni].z;
+      const uint32_t w1 = ks == 0 ? blo[ni].y : ks == 1 ? blo[ni].w : ks == 2 ? bhi[ni].y : bhi[ni].w;
+      bhm[ni][ks] = e4m3x8_to_f16(w0, w1);
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cvt1(0, q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ks = j >> 2, ni = j & 3;
+      const v8h a = (v8h){ap[ks][0][0], ap[ks][0][1], ap[ks][1][0], ap[ks][1][1],
+                          ap[ks][2][0], ap[ks][2][1], ap[ks][3][0], ap[ks][3][1]};
+      tp[ni] = mfma_16x16x32_f16(a, bhm[ni][ks], ks == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : tp[ni]);
+      if (ks < 3) cvt1(ks + 1, ni);
+      if (j >= 2) newb(j - 2);
+      if (j == 8) {
+        alo = *reinterpret_cast<const uint4*>(base + a_off0);
+        ahi = *reinterpret_cast<const uint4*>(base + a_off1);
+        sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    newb(14);
+    newb(15);
+  }
+
   // binary32 scales: the chunk's FP32 sum, then promotion by the vector ALU
   template <int TMA>
   __device__ __forceinline__ void chunk_f32(const uint8_t* base) {
@@ -423,6 +519,46 @@ struct Engine16 {
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
       carry_s = sp;
+    } else if constexpr (DEFER && LATE && IL && C::TN == 4) {
+      // exact products, last row deferred, the instruction order fixed in
+      // the source.  All B fragments are requested first; the previous
+      // chunk's last row runs against the old FP16 B fragments while the new
+      // ones are converted in its shadow, each replacing an old fragment two
+      // matrix operations after the row has read it.
+      uint4 blo[C::TN], bhi[C::TN];
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) {
+        blo[ni] = *reinterpret_cast<const uint4*>(base + b_off0 + ni * 2048);
+        bhi[ni] = *reinterpret_cast<const uint4*>(base + b_off1 + ni * 2048);
+      }
+      uint4 alo, ahi;
+      v4f sa4;
+      v4f tp[C::TN];
+      deferred_interleaved(tp, blo, bhi, base, alo, ahi, sa4);
+      v4f sp = psc;
+      int rp = TMA - 1;  // the row whose promotion is pending
+#pragma unroll
+      for (int mi = 0; mi + 1 < TMA; ++mi) {
+        const uint4 nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+        const uint4 nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+        const v4f nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
+        v4f tc[C::TN];
+        v4f scn;
+        if (rp == TMA - 1) row_interleaved(tc, alo, ahi, acc[TMA - 1], tp, sp, scn, sa4, swv);
+        else row_interleaved(tc, alo, ahi, acc[rp], tp, sp, scn, sa4, swv);
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) tp[ni] = tc[ni];
+        sp = scn;
+        rp = mi;
+        alo = nlo;
+        ahi = nhi;
+        sa4 = nsa;
+      }
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) fma4(acc[rp][ni], tp[ni], sp);
+      pa_lo = alo;
+      pa_hi = ahi;
+      psc = (v4f){sa4[0] * swv, sa4[1] * swv, sa4[2] * swv, sa4[3] * swv};
     } else if constexpr (DEFER) {
       // exact products, last row deferred.  Half the B fragments are
       // requested before the previous chunk's last row runs, the rest after
