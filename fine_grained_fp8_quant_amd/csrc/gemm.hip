@@ -486,6 +486,50 @@ struct Engine16 {
       uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
       uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
       v4f sa4 = *reinterpret_cast<const v4f*>(base + sa_off);
+      if constexpr (IL && C::TN == 4 && !C::SKIP) {
+        // fixed order: each matrix operation (32 cycles) is followed by the
+        // promotion of the previous row's sub-tile in the same column (four
+        // multiply-adds) and one scale product; the first row promotes the
+        // previous chunk's carried row.  Left to itself the compiler issues
+        // a row's four operations back to back and then twenty vector
+        // instructions, and the two waves of a SIMD collide on both.
+        v4f tp[C::TN];
+        v4f sp = carry_s;
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) tp[ni] = carry_t[ni];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = 0; mi < TMA; ++mi) {
+          uint4 nlo = alo, nhi = ahi;
+          v4f nsa = sa4;
+          if (mi + 1 < TMA) {
+            nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+            nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+            nsa = *reinterpret_cast<const v4f*>(base + sa_off + (mi + 1) * 64);
+          }
+          const v8i af = (v8i){(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+          v4f tc[C::TN];
+          v4f sc;
+          const int pr = mi > 0 ? mi - 1 : TMA - 1;  // the row promoted now
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) {
+            tc[ni] = mfma_16x16x128_fp8(af, bf[ni]);
+            fma4(acc[pr][ni], tp[ni], sp);
+            sc[ni] = sa4[ni] * swv;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int ni = 0; ni < C::TN; ++ni) tp[ni] = tc[ni];
+          sp = sc;
+          alo = nlo;
+          ahi = nhi;
+          sa4 = nsa;
+        }
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
+        carry_s = sp;
+        return;
+      }
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) fma4(acc[TMA - 1][ni], carry_t[ni], carry_s);  // the previous chunk's last row
       v4f tp[C::TN];
