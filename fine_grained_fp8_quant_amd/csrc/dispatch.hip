@@ -144,40 +144,54 @@ __global__ __launch_bounds__(64) void k_dispatch_scatter(const int32_t* __restri
   const int lane = threadIdx.x;
   if constexpr (FUSED) {
     int32_t* tot = cnt + E;
-    for (int e = lane; e < E; e += 64) {
-      cnt[e] = 0;
-      tot[e] = 0;
-    }
-    __syncthreads();
-    // the whole count table, 32 independent coalesced loads per lane at a
-    // time; entry idx is block idx / E, expert idx mod E (idx < 2^13, so the
-    // binary32 quotient is within one of the true one and one step fixes it)
-    const int total = nb * E;
-    const float inv_e = 1.0f / (float)E;
-    constexpr int kU = 32;
-    for (int i0 = 0; i0 < total; i0 += 64 * kU) {
-      int32_t c[kU];
+    if (64 % E == 0) {
+      // the table read flat, 64 consecutive entries per load: entry idx
+      // belongs to block idx / E and expert idx mod E, which is lane mod E
+      // for every load; the 64 / E lanes of one expert then add up
+      const int e = lane % E;
+      const int total = nb * E;
+      int32_t all = 0, before = 0;
+      constexpr int kU = 32;
+      for (int i0 = 0; i0 < total; i0 += 64 * kU) {
+        int32_t c[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int idx = i0 + u * 64 + lane;
-        c[u] = idx < total ? base[idx] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int idx = i0 + u * 64 + lane;
-        if (c[u] != 0) {
-          int b = (int)(((float)idx + 0.5f) * inv_e);
-          int e = idx - b * E;
-          if (e < 0) {
-            --b;
-            e += E;
-          } else if (e >= E) {
-            ++b;
-            e -= E;
-          }
-          atomicAdd(&tot[e], c[u]);
-          if (b < (int)blockIdx.x) atomicAdd(&cnt[e], c[u]);
+        for (int u = 0; u < kU; ++u) {
+          const int idx = i0 + u * 64 + lane;
+          c[u] = idx < total ? base[idx] : 0;
         }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int idx = i0 + u * 64 + lane;
+          all += c[u];
+          before += idx / E < (int)blockIdx.x ? c[u] : 0;
+        }
+      }
+      for (int d = E; d < 64; d <<= 1) {
+        all += __shfl_xor(all, d);
+        before += __shfl_xor(before, d);
+      }
+      if (lane < E) {
+        tot[e] = all;
+        cnt[e] = before;
+      }
+    } else {
+      // lane l sums expert e = l (then l + 64, ...) over all blocks and
+      // over the blocks before this one, no atomics
+      for (int e = lane; e < E; e += 64) {
+        int32_t all = 0, before = 0;
+        constexpr int kU = 16;
+        for (int b0 = 0; b0 < nb; b0 += kU) {
+          int32_t c[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) c[u] = b0 + u < nb ? base[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            all += c[u];
+            before += b0 + u < (int)blockIdx.x ? c[u] : 0;
+          }
+        }
+        tot[e] = all;
+        cnt[e] = before;
       }
     }
     __syncthreads();
