@@ -104,13 +104,18 @@ class NoTimer:
 
 
 class Timer:
-    """HIP events around launches on the current stream, summed per name."""
+    """HIP events around launches on the current stream, summed per name
+    (with ``only``: around the launches whose name contains it, the others
+    run untimed)."""
 
-    def __init__(self):
+    def __init__(self, only=None):
         self.pairs = {}
+        self.only = only
 
     def run(self, name, fn):
         import torch
+        if self.only is not None and self.only not in name:
+            return fn()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         out = fn()
@@ -463,10 +468,16 @@ def main():
     # so the step is repeated for PREWARM_S of wall time before the counted
     # warm-up steps, and the timed steps follow the warm-up steps with no host
     # work in between beyond one synchronisation.
-    warm, timer = Timer(), Timer()
-    # A 256-byte device copy on each side of the timed region, outside the
-    # events: in a kernel trace of this run, the dispatches between the two
-    # copies are exactly the timed steps.
+    #
+    # Each HIP event pair around a call adds its markers' processing to the
+    # device timeline (about 5 us per marker on MI355X).  The timed steps
+    # therefore carry events around the GEMM call only (the roofline's
+    # kernel); the per-call times of the other calls come from a second pass
+    # of the same steps right after, with events around every call.
+    timer, calls = Timer(only="gemm"), Timer()
+    # A 256-byte device copy before the timed steps, between them and the
+    # per-call pass, and after it: in a kernel trace of this run, the
+    # dispatches between the first two copies are exactly the timed steps.
     mark = torch.zeros(512, dtype=torch.uint8, device="cuda")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_pre, t_pre = 0, time.perf_counter()
@@ -476,7 +487,7 @@ def main():
             n_pre += 1
         torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i % len(sets), sets[i % len(sets)], warm)
+        step(i % len(sets), sets[i % len(sets)], NoTimer())
     fgq.debug_copy(mark[:256], mark[256:])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -487,14 +498,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fgq.debug_copy(mark[:256], mark[256:])
+    for i in range(args.steps):
+        step(i % len(sets), sets[i % len(sets)], calls)
+    fgq.debug_copy(mark[:256], mark[256:])
     torch.cuda.synchronize()
     print(f"[bench] {n_pre} device warm-up steps, {args.warmup} counted warm-up steps, {len(sets)} input sets",
           file=sys.stderr, flush=True)
     ms_step = start.elapsed_time(end) / args.steps
-    kern = timer.avg_ms()
-    spread = timer.spread_ms()
+    kern = calls.avg_ms()
+    spread = calls.spread_ms()
     last_c = step.outputs[0]["c"]
     gemm_name = [k for k in kern if "gemm" in k][0]
+    # the roofline's kernel: its time in the timed steps themselves
+    kern[gemm_name] = timer.avg_ms()[gemm_name]
+    spread[gemm_name] = timer.spread_ms()[gemm_name]
     gemm_ms = kern[gemm_name]
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     # the contraction's own matrix-core dtype: exact products run on the FP16
@@ -536,8 +553,16 @@ def main():
     # the other GEMM accumulation mode, timed alone (not part of the step)
     other = {"exact": "fp8core", "fp8core": "exact", "promote": "incore", "incore": "promote"}[args.mode]
     alt_step = make_step(args, fgq, d, len(sets), gemm_mode(fgq, other))
-    alt_t = Timer()
-    for i in range(max(3, args.steps // 2)):
+    # the same treatment as the timed steps: a device warm-up in this mode,
+    # then the steps with events around the GEMM call only
+    n_alt, t_alt = 0, time.perf_counter()
+    while time.perf_counter() - t_alt < PREWARM_S / 2:
+        for _ in range(4):
+            alt_step(n_alt % len(sets), sets[n_alt % len(sets)], NoTimer())
+            n_alt += 1
+        torch.cuda.synchronize()
+    alt_t = Timer(only="gemm")
+    for i in range(args.steps):
         alt_step(i % len(sets), sets[i % len(sets)], alt_t)
     torch.cuda.synchronize()
     alt_ms = alt_t.avg_ms()[gemm_name]
@@ -577,6 +602,9 @@ def main():
         "cpu_baseline": cpu,
         "accuracy": accuracy,
         "ceilings": ceilings,
+        "timing": "value and ms_per_step: the timed steps, HIP events around the GEMM call only; kernels: the "
+                  "GEMM's per-call time from those steps, the other calls' from a second pass of the same steps "
+                  "with events around every call (each event marker adds about 5 us of device time)",
         "wall_s_timed": wall,
     }
     print(json.dumps(line), flush=True)

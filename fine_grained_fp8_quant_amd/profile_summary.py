@@ -131,20 +131,43 @@ def read_pmc(path):
     return [(k, v) for _, k, v in out]
 
 
-def read_trace_timed(path):
+def read_trace_timed(path, spans=False):
     """(kernel, duration us) of every dispatch between the first two marker
-    copies (k_debug_copy) of a kernel trace, in dispatch order; None when the
-    trace holds fewer than two markers."""
+    copies (k_debug_copy) of a kernel trace, in dispatch order (with
+    ``spans``: (kernel, start us, end us)); None when the trace holds fewer
+    than two markers."""
     rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
-            rows.append((int(r["Dispatch_Id"]), short(r["Kernel_Name"]),
-                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+            rows.append((int(r["Dispatch_Id"]), short(r["Kernel_Name"]), int(r["Start_Timestamp"]) / 1e3,
+                         int(r["End_Timestamp"]) / 1e3))
     rows.sort()
-    marks = [i for i, (_, k, _) in enumerate(rows) if k.startswith("k_debug_copy")]
+    marks = [i for i, row in enumerate(rows) if row[1].startswith("k_debug_copy")]
     if len(marks) < 2:
         return None
-    return [(k, us) for _, k, us in rows[marks[0] + 1:marks[1]]]
+    timed = rows[marks[0] + 1:marks[1]]
+    if spans:
+        return [(k, t0, t1) for _, k, t0, t1 in timed]
+    return [(k, t1 - t0) for _, k, t0, t1 in timed]
+
+
+def call_spans(timed, e8, mode):
+    """Average span (first kernel's start to last kernel's end, us) of each
+    C-ABI call in the timed dispatches, consecutive kernels of one call
+    grouped; kernels that carry no mode belong to ``mode``."""
+    spans = defaultdict(list)
+    cur, t_start, t_end = None, 0.0, 0.0
+    for k, t0, t1 in timed:
+        api, md = api_of(k, e8)
+        key = None if api is None else api + (f"[{md or mode}]" if "gemm" in api and (md or mode) else "")
+        if key != cur:
+            if cur is not None:
+                spans[cur].append(t_end - t_start)
+            cur, t_start = key, t0
+        t_end = t1
+    if cur is not None:
+        spans[cur].append(t_end - t_start)
+    return {k: sum(v) / len(v) for k, v in spans.items() if k is not None}
 
 
 def read_counters(path):
@@ -243,6 +266,7 @@ def summarise(out_dir, spec, traffic):
         return per_call
 
     if timed is not None:
+        mode = bench.get("gemm_mode") if bench else None
         tk = defaultdict(list)
         for k, us in timed:
             tk[k].append(us)
@@ -250,17 +274,16 @@ def summarise(out_dir, spec, traffic):
                   "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
         for k, v in sorted(tk.items(), key=lambda kv: -sum(kv[1])):
             lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
-        per_call = per_call_table([(k, sum(v) / len(v)) for k, v in tk.items()])
-        lines += ["", "Per call over the timed steps (sum of the average durations of the call's kernels):", "",
-                  "| call | avg us |", "|---|---|"]
-        for key in sorted(per_call):
-            lines.append(f"| {key} | {per_call[key]:.1f} |")
+        spans = call_spans(read_trace_timed(os.path.join(tdir, "trace_kernel_trace.csv"), spans=True), e8, mode)
+        lines += ["", "Per call over the timed steps: the span from the call's first kernel start to its last kernel "
+                  "end (what HIP events around the call measure, gaps between its kernels included):", "",
+                  "| call | avg span us |", "|---|---|"]
+        for key in sorted(spans):
+            lines.append(f"| {key} | {spans[key]:.1f} |")
         if bench:
             rf = bench["roofline"]
             gk = rf["kernel"]
-            mode = bench.get("gemm_mode")
-            gemm_api = [key for key in per_call if key.startswith(("gemm", "grouped")) and
-                        (key.endswith(f"[{mode}]") or "[" not in key)]
+            gemm_api = [key for key in spans if key.startswith(("gemm", "grouped")) and key.endswith(f"[{mode}]")]
             ms_ev = bench["kernels"][gk]["ms"]
             lines += ["", "## The bench line of the traced run", "",
                       f"    roofline: bound {rf['bound']}, achieved {rf['achieved']:.1f} {rf['unit']}, "
@@ -268,7 +291,7 @@ def summarise(out_dir, spec, traffic):
                       f"    {gk}: {ms_ev * 1e3:.1f} us per call (HIP events); "
                       f"ms_per_step {bench['ms_per_step']:.4f}", ""]
             if gemm_api:
-                us_tr = per_call[gemm_api[0]]
+                us_tr = spans[gemm_api[0]]
                 frac_tr = rf["frac"] * (ms_ev * 1e3) / us_tr
                 lines += [f"Recomputed from the trace: {gemm_api[0]} {us_tr:.1f} us per call, so frac = "
                           f"{rf['frac']:.4f} x {ms_ev * 1e3:.1f} / {us_tr:.1f} = {frac_tr:.4f} "

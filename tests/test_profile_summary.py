@@ -73,3 +73,14 @@ def test_utilisation_ratios(tmp_path):
     assert abs(got["co-issue / MFMA busy"] - 0.25) < 1e-12
     assert abs(got["VALU inst / MFMA inst"] - 2.5) < 1e-12
     assert abs(got["L2 hit"] - 0.75) < 1e-12
+
+
+def test_call_spans_group_consecutive_kernels_of_one_call():
+    from fine_grained_fp8_quant_amd.profile_summary import call_spans
+    timed = [("k_quant_act_1x128<ScaleF32>", 0.0, 3.0),
+             ("k_gemm_fp8_bs_splitk[64x128,exact]", 4.0, 34.0), ("k_splitk_reduce", 38.0, 42.0),
+             ("k_quant_act_1x128<ScaleF32>", 50.0, 53.0),
+             ("k_gemm_fp8_bs_splitk[64x128,exact]", 54.0, 84.0), ("k_splitk_reduce", 86.0, 90.0)]
+    sp = call_spans(timed, False, "exact")
+    assert sp["gemm_fp8_blockscaled[exact]"] == 37.0  # (42 - 4 + 90 - 54) / 2
+    assert sp["quant_act_1x128"] == 3.0
