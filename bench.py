@@ -103,6 +103,36 @@ class NoTimer:
         return fn()
 
 
+class Collect:
+    """Runs the launches and keeps each one, per name, for replay."""
+
+    def __init__(self):
+        self.fns = {}
+
+    def run(self, name, fn):
+        self.fns.setdefault(name, []).append(fn)
+        return fn()
+
+
+def time_back_to_back(fns, n, groups=5):
+    """Per-call milliseconds of the calls in ``fns`` (one per input set, used in
+    turn): ``groups`` groups of ``n`` back-to-back calls, one HIP event pair
+    per group, so the events' own device time is spread over n calls.
+    Returns (mean, p10, median, p90) over the groups."""
+    import torch
+    pairs = []
+    for _ in range(groups):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for j in range(n):
+            fns[j % len(fns)]()
+        e.record()
+        pairs.append((s, e))
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) / n for s, e in pairs])
+    return float(t.mean()), float(np.percentile(t, 10)), float(np.median(t)), float(np.percentile(t, 90))
+
+
 class Timer:
     """HIP events around launches on the current stream, summed per name
     (with ``only``: around the launches whose name contains it, the others
@@ -474,7 +504,7 @@ def main():
     # therefore carry events around the GEMM call only (the roofline's
     # kernel); the per-call times of the other calls come from a second pass
     # of the same steps right after, with events around every call.
-    timer, calls = Timer(only="gemm"), Timer()
+    timer = Timer(only="gemm")
     # A 256-byte device copy before the timed steps, between them and the
     # per-call pass, and after it: in a kernel trace of this run, the
     # dispatches between the first two copies are exactly the timed steps.
@@ -498,18 +528,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fgq.debug_copy(mark[:256], mark[256:])
-    for i in range(args.steps):
-        step(i % len(sets), sets[i % len(sets)], calls)
+    # the other calls: back-to-back groups over the input sets (each group's
+    # calls read different sets in turn, as the steps do)
+    col = Collect()
+    for i in range(len(sets)):
+        step(i, sets[i], col)
+    calls = {name: time_back_to_back(fns, max(4, args.steps // 4)) for name, fns in col.fns.items()
+             if "gemm" not in name}
     fgq.debug_copy(mark[:256], mark[256:])
     torch.cuda.synchronize()
     print(f"[bench] {n_pre} device warm-up steps, {args.warmup} counted warm-up steps, {len(sets)} input sets",
           file=sys.stderr, flush=True)
     ms_step = start.elapsed_time(end) / args.steps
-    kern = calls.avg_ms()
-    spread = calls.spread_ms()
+    kern = {name: v[0] for name, v in calls.items()}
+    spread = {name: {"p10": v[1], "median": v[2], "p90": v[3]} for name, v in calls.items()}
     last_c = step.outputs[0]["c"]
-    gemm_name = [k for k in kern if "gemm" in k][0]
     # the roofline's kernel: its time in the timed steps themselves
+    gemm_name = [k for k in timer.avg_ms() if "gemm" in k][0]
     kern[gemm_name] = timer.avg_ms()[gemm_name]
     spread[gemm_name] = timer.spread_ms()[gemm_name]
     gemm_ms = kern[gemm_name]
@@ -602,9 +637,10 @@ def main():
         "cpu_baseline": cpu,
         "accuracy": accuracy,
         "ceilings": ceilings,
-        "timing": "value and ms_per_step: the timed steps, HIP events around the GEMM call only; kernels: the "
-                  "GEMM's per-call time from those steps, the other calls' from a second pass of the same steps "
-                  "with events around every call (each event marker adds about 5 us of device time)",
+        "timing": "value and ms_per_step: the timed steps, HIP events around the GEMM call only (each event "
+                  "marker adds about 5 us of device time); kernels: the GEMM's per-call time from those steps, "
+                  "each other call's from five groups of back-to-back calls over the input sets, one event pair "
+                  "per group (mean; p10 / median / p90 over the groups)",
         "wall_s_timed": wall,
     }
     print(json.dumps(line), flush=True)
