@@ -282,6 +282,42 @@ struct Engine16 {
     uint4 alo = *reinterpret_cast<const uint4*>(base + a_off0);
     uint4 ahi = *reinterpret_cast<const uint4*>(base + a_off1);
     int sav = base[a_byte];
+    if constexpr (MODE == 2 && IL && C::TN == 4 && !C::SKIP) {
+      // fixed order, as in the FP8-core rows: each matrix operation is
+      // followed by the previous row's four adds in its column; the first
+      // row adds the previous chunk's carried row
+      v4f tp[C::TN];
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) tp[ni] = carry_t[ni];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mi = 0; mi < TMA; ++mi) {
+        uint4 nlo = alo, nhi = ahi;
+        int nsa = sav;
+        if (mi + 1 < TMA) {
+          nlo = *reinterpret_cast<const uint4*>(base + a_off0 + (mi + 1) * 2048);
+          nhi = *reinterpret_cast<const uint4*>(base + a_off1 + (mi + 1) * 2048);
+          nsa = base[a_byte + (mi + 1) * 64];
+        }
+        const v8i af = (v8i){(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+        const int pr = mi > 0 ? mi - 1 : TMA - 1;  // the row added now
+        v4f tc[C::TN];
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) {
+          tc[ni] = mfma_16x16x128_fp8_e8m0(af, bf[ni], (v4f){0.0f, 0.0f, 0.0f, 0.0f}, sav, swv);
+          add4(acc[pr][ni], tp[ni]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ni = 0; ni < C::TN; ++ni) tp[ni] = tc[ni];
+        alo = nlo;
+        ahi = nhi;
+        sav = nsa;
+      }
+#pragma unroll
+      for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
+      return;
+    }
     if constexpr (MODE == 2) {
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) add4(acc[TMA - 1][ni], carry_t[ni]);  // the previous chunk's last row
