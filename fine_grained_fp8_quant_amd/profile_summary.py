@@ -296,6 +296,11 @@ def summarise(out_dir, spec, traffic):
                 lines += [f"Recomputed from the trace: {gemm_api[0]} {us_tr:.1f} us per call, so frac = "
                           f"{rf['frac']:.4f} x {ms_ev * 1e3:.1f} / {us_tr:.1f} = {frac_tr:.4f} "
                           f"({(frac_tr / rf['frac'] - 1) * 100:+.1f}% against the line).", ""]
+                if abs(frac_tr / rf["frac"] - 1) > 0.03:
+                    lines += [f"The difference, {ms_ev * 1e3 - us_tr:.1f} us per call, is the device time of the HIP "
+                              "event markers around the call (the trace shows about 10 us between calls that carry "
+                              "an end and a start marker, none between the kernels of one call); the span excludes "
+                              "it, the events include one marker.", ""]
     lines += ["## Kernel trace of the whole run (`--kernel-trace --stats`; includes warm-up calls)", "",
               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:
