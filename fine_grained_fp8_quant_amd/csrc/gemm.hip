@@ -208,6 +208,11 @@ struct Engine16 {
   // (FP16), the row's A codes and its promotion scales.  Every accumulator
   // still takes its chunk terms in chunk order.
   static constexpr bool DEFER = MODE == 0 && !C::SKIP;
+  // The fixed-order exact path takes the next chunk's DMA request as a hook
+  // and issues it after the deferred row, not before the chunk's first LDS
+  // read (1-2% shorter on the grouped and dense prefill shapes: the request
+  // then queues behind the fragment reads instead of in front of them).
+  static constexpr bool ISSUE_IN_CHUNK = DEFER && LATE && IL && C::TN == 4;
   v8h bhm[C::TN][4];
   uint4 pa_lo, pa_hi;
   v4f psc;
@@ -260,10 +265,12 @@ struct Engine16 {
   }
 
   // TMA: sub-tile rows that hold rows of the tile (the rest are skipped)
-  template <int TMA = C::TM>
-  __device__ __forceinline__ void chunk(const uint8_t* base, int kb) {
+  // With ISSUE_IN_CHUNK, `issue` (callable, no arguments) is run exactly
+  // once inside the chunk; otherwise it must be null.
+  template <int TMA = C::TM, class F = int>
+  __device__ __forceinline__ void chunk(const uint8_t* base, int kb, F* issue = nullptr) {
     if constexpr (MODE >= 2) chunk_e8m0<TMA>(base, kb);
-    else chunk_f32<TMA>(base);
+    else chunk_f32<TMA>(base, issue);
   }
 
   // E8M0: one scale byte per sub-tile row (this lane's row l16) and one per
@@ -505,8 +512,8 @@ struct Engine16 {
   }
 
   // binary32 scales: the chunk's FP32 sum, then promotion by the vector ALU
-  template <int TMA>
-  __device__ __forceinline__ void chunk_f32(const uint8_t* base) {
+  template <int TMA, class F = int>
+  __device__ __forceinline__ void chunk_f32(const uint8_t* base, F* issue = nullptr) {
     const float swv = reinterpret_cast<const float*>(base + C::SW_OFF)[sw_idx];
     if constexpr (MODE == 1) {
       // FP8 matrix core: one instruction per 16x16 sub-tile and chunk
@@ -599,7 +606,7 @@ struct Engine16 {
 #pragma unroll
       for (int ni = 0; ni < C::TN; ++ni) carry_t[ni] = tp[ni];
       carry_s = sp;
-    } else if constexpr (DEFER && LATE && IL && C::TN == 4) {
+    } else if constexpr (ISSUE_IN_CHUNK) {
       // exact products, last row deferred, the instruction order fixed in
       // the source.  All B fragments are requested first; the previous
       // chunk's last row runs against the old FP16 B fragments while the new
@@ -615,6 +622,7 @@ struct Engine16 {
       v4f sa4;
       v4f tp[C::TN];
       deferred_interleaved(tp, blo, bhi, base, alo, ahi, sa4);
+      if constexpr (!std::is_same<F, int>::value) (*issue)();
       v4f sp = psc;
       int rp = TMA - 1;  // the row whose promotion is pending
 #pragma unroll
@@ -889,8 +897,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
       if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
       barrier_no_drain();
-      if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-      if constexpr (decltype(tma)::value > 0) eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
+      auto next = [&]() {
+        if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
+      };
+      if constexpr (decltype(eng)::ISSUE_IN_CHUNK && decltype(tma)::value > 0) {
+        eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb, &next);
+      } else {
+        next();
+        if constexpr (decltype(tma)::value > 0) eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
+      }
     }
     if constexpr (decltype(tma)::value > 0) eng.template flush<decltype(tma)::value>();
   };
