@@ -290,6 +290,13 @@ def summarise(out_dir, spec, traffic):
                       f"peak {rf['peak']}, frac {rf['frac']:.4f}",
                       f"    {gk}: {ms_ev * 1e3:.1f} us per call (HIP events); "
                       f"ms_per_step {bench['ms_per_step']:.4f}", ""]
+            ce = bench.get("ceilings") or {}
+            if "mfma_fp8_tflops" in ce and "mfma_fp16_tflops" in ce:
+                # boxes differ by several percent in clock; the loop rates of
+                # the same run say which kind of box the trace came from
+                lines += [f"Matrix-core loop rates of the same run (register-only, two waves per SIMD): FP8 "
+                          f"{ce['mfma_fp8_tflops']:.0f} TFLOP/s at {ce['mfma_fp8_sclk_ghz']:.2f} GHz, FP16 "
+                          f"{ce['mfma_fp16_tflops']:.0f} TFLOP/s at {ce['mfma_fp16_sclk_ghz']:.2f} GHz.", ""]
             if gemm_api:
                 us_tr = spans[gemm_api[0]]
                 frac_tr = rf["frac"] * (ms_ev * 1e3) / us_tr
