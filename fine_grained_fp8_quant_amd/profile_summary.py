@@ -151,6 +151,13 @@ def read_trace_timed(path, spans=False):
     return [(k, t1 - t0) for _, k, t0, t1 in timed]
 
 
+def call_key(kname, e8, mode):
+    """The C-ABI call a kernel belongs to (GEMMs with their mode), or None;
+    kernels that carry no mode belong to ``mode``."""
+    api, md = api_of(kname, e8)
+    return None if api is None else api + (f"[{md or mode}]" if "gemm" in api and (md or mode) else "")
+
+
 def call_spans(timed, e8, mode):
     """Average span (first kernel's start to last kernel's end, us) of each
     C-ABI call in the timed dispatches, consecutive kernels of one call
@@ -158,8 +165,7 @@ def call_spans(timed, e8, mode):
     spans = defaultdict(list)
     cur, t_start, t_end = None, 0.0, 0.0
     for k, t0, t1 in timed:
-        api, md = api_of(k, e8)
-        key = None if api is None else api + (f"[{md or mode}]" if "gemm" in api and (md or mode) else "")
+        key = call_key(k, e8, mode)
         if key != cur:
             if cur is not None:
                 spans[cur].append(t_end - t_start)
@@ -168,6 +174,27 @@ def call_spans(timed, e8, mode):
     if cur is not None:
         spans[cur].append(t_end - t_start)
     return {k: sum(v) / len(v) for k, v in spans.items() if k is not None}
+
+
+def call_gaps(timed, e8, mode, target):
+    """Average idle time (us) of the GPU in the timed dispatches: right before
+    the first kernel of each ``target`` call, right after its last, and
+    between consecutive kernels that are not at its edges.  None where no
+    such gap occurs."""
+    before, after, other = [], [], []
+    prev_key, prev_end = None, None
+    for k, t0, t1 in timed:
+        key = call_key(k, e8, mode)
+        if prev_end is not None:
+            gap = t0 - prev_end
+            if key == target and prev_key != target:
+                before.append(gap)
+            elif prev_key == target and key != target:
+                after.append(gap)
+            elif key != target and prev_key != target:
+                other.append(gap)
+        prev_key, prev_end = key, t1
+    return tuple(sum(v) / len(v) if v else None for v in (before, after, other))
 
 
 def read_counters(path):
@@ -274,7 +301,8 @@ def summarise(out_dir, spec, traffic):
                   "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
         for k, v in sorted(tk.items(), key=lambda kv: -sum(kv[1])):
             lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
-        spans = call_spans(read_trace_timed(os.path.join(tdir, "trace_kernel_trace.csv"), spans=True), e8, mode)
+        timed_spans = read_trace_timed(os.path.join(tdir, "trace_kernel_trace.csv"), spans=True)
+        spans = call_spans(timed_spans, e8, mode)
         lines += ["", "Per call over the timed steps: the span from the call's first kernel start to its last kernel "
                   "end (what HIP events around the call measure, gaps between its kernels included):", "",
                   "| call | avg span us |", "|---|---|"]
@@ -304,10 +332,13 @@ def summarise(out_dir, spec, traffic):
                           f"{rf['frac']:.4f} x {ms_ev * 1e3:.1f} / {us_tr:.1f} = {frac_tr:.4f} "
                           f"({(frac_tr / rf['frac'] - 1) * 100:+.1f}% against the line).", ""]
                 if abs(frac_tr / rf["frac"] - 1) > 0.03:
-                    lines += [f"The difference, {ms_ev * 1e3 - us_tr:.1f} us per call, is the device time of the HIP "
-                              "event markers around the call (the trace shows about 10 us between calls that carry "
-                              "an end and a start marker, none between the kernels of one call); the span excludes "
-                              "it, the events include one marker.", ""]
+                    g0, g1, go = call_gaps(timed_spans, e8, mode, gemm_api[0])
+                    fmt = lambda g: "-" if g is None else f"{g:.1f} us"
+                    lines += [f"The difference, {ms_ev * 1e3 - us_tr:.1f} us per call, lies outside the call's "
+                              f"kernels: in this trace the GPU idles {fmt(g0)} before the call's first kernel and "
+                              f"{fmt(g1)} after its last, where the HIP event markers of the timed call are "
+                              f"processed, against {fmt(go)} on average between the other kernels of a step. The "
+                              "events include that processing, the span does not.", ""]
     lines += ["## Kernel trace of the whole run (`--kernel-trace --stats`; includes warm-up calls)", "",
               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in stats:

@@ -84,3 +84,16 @@ def test_call_spans_group_consecutive_kernels_of_one_call():
     sp = call_spans(timed, False, "exact")
     assert sp["gemm_fp8_blockscaled[exact]"] == 37.0  # (42 - 4 + 90 - 54) / 2
     assert sp["quant_act_1x128"] == 3.0
+
+
+def test_call_gaps_split_edges_of_the_target_call_from_the_rest():
+    from fine_grained_fp8_quant_amd.profile_summary import call_gaps
+    timed = [("k_quant_act_1x128<ScaleF32>", 0.0, 3.0),
+             ("k_gemm_fp8_bs_splitk[64x128,exact]", 8.0, 34.0), ("k_splitk_reduce", 34.0, 42.0),
+             ("k_quant_act_1x128<ScaleF32>", 46.0, 49.0), ("k_quant_w_128x128<ScaleF32, false>", 50.0, 60.0),
+             ("k_gemm_fp8_bs_splitk[64x128,exact]", 66.0, 84.0), ("k_splitk_reduce", 84.0, 90.0)]
+    before, after, other = call_gaps(timed, False, "exact", "gemm_fp8_blockscaled[exact]")
+    assert before == 5.5      # (8 - 3 + 66 - 60) / 2
+    assert after == 4.0       # 46 - 42
+    assert other == 1.0       # 50 - 49; the gaps inside the call are not counted
+    assert call_gaps(timed[:1], False, "exact", "gemm_fp8_blockscaled[exact]") == (None, None, None)
