@@ -208,10 +208,12 @@ struct Engine16 {
   // (FP16), the row's A codes and its promotion scales.  Every accumulator
   // still takes its chunk terms in chunk order.
   static constexpr bool DEFER = MODE == 0 && !C::SKIP;
-  // The fixed-order exact path takes the next chunk's DMA request as a hook
-  // and issues it after the deferred row, not before the chunk's first LDS
-  // read (1-2% shorter on the grouped and dense prefill shapes: the request
-  // then queues behind the fragment reads instead of in front of them).
+  // The fixed-order exact path takes the B part of the next chunk's DMA
+  // request as a hook and issues it after the deferred row; the A codes and
+  // scales still go out at the chunk top.  The larger B request then queues
+  // behind the chunk's fragment reads instead of in front of them (about 2%
+  // shorter than issuing everything at the top, on the dense and grouped
+  // prefill shapes).
   static constexpr bool ISSUE_IN_CHUNK = DEFER && LATE && IL && C::TN == 4;
   v8h bhm[C::TN][4];
   uint4 pa_lo, pa_hi;
@@ -853,14 +855,22 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
     s_src = sw + ((n0 >> 7) + (lane < C::NBW ? lane : 0)) * sw_snb;
   }
 
-  auto issue = [&](int kb, int stage) {
+  // what: kDmaAll, or the two parts of a split request, kDmaA (A codes and
+  // both scale slots) and kDmaB (B codes)
+  constexpr int kDmaAll = 0, kDmaA = 1, kDmaB = 2;
+  auto issue = [&](int kb, int stage, int what = kDmaAll) {
     uint8_t* base = lds + stage * C::STAGE;
     const uint8_t* at = a_tile + (int64_t)kb * 128;
     const uint8_t* bt = b_tile + (int64_t)kb * 128;
+    if (what != kDmaB) {
 #pragma unroll
-    for (int j = 0; j < C::A_PER_W; ++j) dma16(at + a_src[j], base + (wave + j * C::NW) * 1024);
+      for (int j = 0; j < C::A_PER_W; ++j) dma16(at + a_src[j], base + (wave + j * C::NW) * 1024);
+    }
+    if (what != kDmaA) {
 #pragma unroll
-    for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
+      for (int j = 0; j < C::B_PER_W; ++j) dma16(bt + b_src[j], base + C::A_BYTES + (wave + j * C::NW) * 1024);
+    }
+    if (what == kDmaB) return;
     if (wave < C::SA_INS) {
       dma4(word_of(s_src + (int64_t)kb * sa_skb), base + C::SA_OFF + wave * 256);
     } else if (wave == C::SA_INS) {
@@ -897,13 +907,18 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, int64_
       if (kb + C::NSTAGE - 2 < kb_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds((C::NSTAGE - 2) * C::DMA_PER_CHUNK));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lds(0));
       barrier_no_drain();
-      auto next = [&]() {
-        if (kb + C::NSTAGE - 1 < kb_end) issue(kb + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-      };
+      // every part of chunk kb + NSTAGE - 1's request goes out in this
+      // iteration, so the wait at the top of the next one counts as before
+      const bool more = kb + C::NSTAGE - 1 < kb_end;
+      const int nstage = (it + C::NSTAGE - 1) % C::NSTAGE;
       if constexpr (decltype(eng)::ISSUE_IN_CHUNK && decltype(tma)::value > 0) {
-        eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb, &next);
+        if (more) issue(kb + C::NSTAGE - 1, nstage, kDmaA);
+        auto rest = [&]() {
+          if (more) issue(kb + C::NSTAGE - 1, nstage, kDmaB);
+        };
+        eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb, &rest);
       } else {
-        next();
+        if (more) issue(kb + C::NSTAGE - 1, nstage);
         if constexpr (decltype(tma)::value > 0) eng.template chunk<decltype(tma)::value>(lds + stage * C::STAGE, kb);
       }
     }
