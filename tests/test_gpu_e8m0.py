@@ -126,7 +126,7 @@ def test_quant_w_e8m0(fgq_gpu, shape):
     _same(q.cpu().numpy(), s.cpu().numpy(), qo, so, f"w e8m0 {shape}")
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (5, 640), (33, 2048), (7, 7168), (3, 16384)])
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 640), (33, 2048), (7, 7168), (4103, 7168), (3, 16384)])
 def test_fused_rmsnorm_e8m0(fgq_gpu, M, K):
     import torch
     log(f"fused_rmsnorm_quant_e8m0 {M}x{K}")

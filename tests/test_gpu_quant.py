@@ -240,6 +240,17 @@ def test_fused_workload_rows(fgq_gpu):
     _assert_same(q, s, qo, so, "fused 1027x7168")
 
 
+@pytest.mark.parametrize("scale_t", [False, True])
+def test_fused_many_rows_ragged(fgq_gpu, scale_t):
+    # 4103 rows at K 7168, every row against the oracle: 1026 workgroups of
+    # four rows, the last holding three (its fourth wave loads nothing and
+    # stores nothing), with row-major and K-block-major scales
+    d = make_workload("fused_down", rows=4103, parts={"X", "gamma"})
+    q, s = _fused(fgq_gpu, d["X"], d["gamma"], d["eps"], scale_t=scale_t)
+    qo, so = oracle.fused_rmsnorm_quant(d["X"], d["gamma"], d["eps"])
+    _assert_same(q, s, qo, so, f"fused 4103x7168 scale_t={scale_t}")
+
+
 def test_fused_full_size_sampled_rows(fgq_gpu):
     import torch
     d = make_workload("fused_down", parts={"X", "gamma"})
