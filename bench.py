@@ -20,9 +20,11 @@ scale bytes, applied by the FP8 matrix core); --mode then picks how the GEMM
 accumulates (promote: per-chunk FP32 promotion; incore: in the matrix core).
 Inputs rotate over several buffer sets so the 256 MB last-level cache
 cannot serve one step from the previous one.  `value` is whole-step GEMM
-throughput: GEMM FLOPs per step / step time.  Per-kernel durations come
-from HIP events recorded around each launch on the launch stream inside the
-timed region.  Rank 0 prints one JSON line.
+throughput: GEMM FLOPs per step / step time.  The GEMM's per-call time comes
+from fence-free HIP events around the GEMM call, on its launch stream, in
+every timed step; each other call is timed after the timed steps in groups
+of back-to-back calls, one event pair per group.  The one process prints one
+JSON line.
 """
 from __future__ import annotations
 
